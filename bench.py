@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark: one pass of the UniPrefill pruning path on MI355X.
+
+A step is the whole hot path over one packed batch already resident in HBM:
+up_score (tail-query scores + block means) -> up_select_topp (Top-p mask) ->
+up_compact (gather of kept rows) -> up_drop_history (ledger append).
+
+Default workload: Llama-3.1-8B-shaped full-attention layer, one request of
+L = 131072 tokens, 32 q / 8 KV heads, head_dim 128, hidden 4096 bf16, n=128,
+G=64, p=0.99, 128 sink / 128 tail tokens, 5% planted blocks (seeded).
+
+Prints ONE JSON line (rank 0).  Besides the required fields it reports the
+roofline of the dominant kernel (HIP events on the stream the kernels run
+on), a per-call time breakdown, the scoring kernels' MFMA fraction, and the
+CPU oracle timed on the host on the same input bytes (with a full-size parity
+check of the GPU result against it).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s of score+select+compact at L=128K; % MFMA peak, % HBM peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "token_block_sparsification_amd", "csrc")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_L131072")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (for profiler runs)")
+    ap.add_argument("--cpu-threads", type=int, default=1,
+                    help="BLAS threads the oracle may use")
+    return ap.parse_args()
+
+
+def source_sha(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str, src: str, launches_per_call: int = 1):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    the kernel's source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the head-parallel design is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import token_block_sparsification_amd as U
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (no HIP device visible)")
+    U.lib()  # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = W.get_workload(args.workload)
+    t_gen = time.perf_counter()
+    inp = W.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    batch = U.Batch.make(inp["cu_seqlens"], w.block, dev)
+    q, k, hidden, pos = inp["q"], inp["k"], inp["hidden"], inp["positions"]
+    ws = U.Workspace.make(batch, w.hq, w.hkv, w.head_dim, w.n_query, hidden, dev)
+    cap = 64
+    ledger = torch.empty(U.up_history_bytes(batch.num_seqs, cap) // 4, dtype=torch.int32,
+                         device=dev)
+    U.up_history_init(ledger, batch.num_seqs, cap)
+    T, N, B = batch.num_tokens, batch.num_blocks, batch.num_seqs
+
+    def step(ev=None, layer=0):
+        if ev is not None:
+            ev[0].record()
+        U.up_score(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, q, k, w.n_query,
+                   w.block, 0.0, ws.token_scores, ws.block_scores, ws.score_ws)
+        if ev is not None:
+            ev[1].record()
+        U.up_select_topp(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d,
+                         ws.block_scores, w.block, w.top_p, w.sink, w.tail, ws.block_mask,
+                         ws.kept_tokens)
+        if ev is not None:
+            ev[2].record()
+        U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, w.block,
+                     ws.block_mask, hidden, pos, ws.hidden_out, ws.positions_out,
+                     ws.cu_seqlens_out, ws.compact_ws)
+        if ev is not None:
+            ev[3].record()
+        U.up_drop_history(ledger, B, cap, layer % cap, ws.cu_seqlens_out)
+        if ev is not None:
+            ev[4].record()
+
+    for i in range(args.warmup):
+        step(layer=i)
+        U.up_history_init(ledger, B, cap)
+    torch.cuda.synchronize()
+    kept = int(ws.cu_seqlens_out[-1].item())
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    U.up_history_init(ledger, B, cap)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i], layer=i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    names = ["up_score", "up_select_topp", "up_compact", "up_drop_history"]
+    per_call_us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(K)])) * 1e3
+                   for j, n in enumerate(names)}
+    tokens_per_s = T / (ms_per_step / 1e3)
+
+    # --- algorithmic work -------------------------------------------------
+    lens = [int(x) for x in inp["lengths"]]
+    pairs = 0
+    for L in lens:
+        ne = min(w.n_query, L)
+        pairs += ne * L - ne * (ne - 1) // 2          # causal-visible (row, key) pairs per head
+    flops_alg = 2.0 * w.head_dim * w.hq * pairs        # one Q K^T over visible pairs
+    flops_exec = 2.0 * flops_alg                       # exact column sums recompute S once
+    row_bytes = hidden[0].numel() * hidden.element_size()
+    compact_bytes = 2 * kept * row_bytes + 2 * 4 * kept + N
+    score_bytes = T * w.hkv * w.head_dim * 2 + sum(min(w.n_query, L) for L in lens) * w.hq * w.head_dim * 2
+
+    t_score = per_call_us["up_score"] * 1e-6
+    t_compact = per_call_us["up_compact"] * 1e-6
+    t_select = per_call_us["up_select_topp"] * 1e-6
+    compact_gbs = compact_bytes / t_compact / 1e9
+    score_tflops_exec = flops_exec / t_score / 1e12
+    score_tflops_alg = flops_alg / t_score / 1e12
+
+    if t_compact >= t_score:
+        traffic = load_traffic("up_compact_kernel", "up_compact.hip")
+        roofline = {"kernel": "up_compact_kernel", "bound": "hbm", "achieved": round(compact_gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
+                    "traffic": traffic,
+                    "algorithmic_bytes_per_launch": int(compact_bytes)}
+    else:
+        roofline = {"kernel": "up_score (rowstats+combine+colsum+blockmean)", "bound": "mfma",
+                    "achieved": round(score_tflops_exec, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(score_tflops_exec / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None, "algorithmic_flops_per_launch": flops_exec}
+
+    rec = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": B, "tokens": T, "seq_len": max(lens),
+                   "hq": w.hq, "hkv": w.hkv, "head_dim": w.head_dim, "n_query": w.n_query,
+                   "block": w.block, "top_p": w.top_p, "sink": w.sink, "tail": w.tail,
+                   "hidden_dim": w.hidden_dim, "hidden_dtype": w.hidden_dtype,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "breakdown_us": {k2: round(v, 2) for k2, v in per_call_us.items()},
+        "score_mfma": {"executed_tflops": round(score_tflops_exec, 1),
+                       "algorithmic_tflops": round(score_tflops_alg, 1),
+                       "frac_of_peak_executed": round(score_tflops_exec / PEAK_BF16_TFLOPS, 4),
+                       "frac_of_peak_algorithmic": round(score_tflops_alg / PEAK_BF16_TFLOPS, 4),
+                       "executed_flops_per_call": flops_exec, "k_bytes_per_call": int(score_bytes)},
+        "select_compact_hbm": {"bytes": int(compact_bytes + 5 * N),
+                               "gbs": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9, 1),
+                               "frac_of_peak": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9 / PEAK_HBM_GBS, 4)},
+        "keep_ratio": round(kept / T, 5),
+        "input_generation_s": round(t_gen, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"], rec["parity"] = cpu_leg(w, inp, ws, kept, args.cpu_threads, T)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_leg(w, inp, ws, kept, threads, T):
+    """Time the CPU oracle on the same input bytes and check the GPU result."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    cu = inp["cu_seqlens"].numpy()
+    lens = inp["lengths"]
+    q_bits = inp["q"].view(torch.int16)
+    q64 = np.zeros(tuple(inp["q"].shape), dtype=np.float64)   # untouched pages stay virtual
+    for r, L in enumerate(lens):
+        ne = min(w.n_query, L)
+        s1 = int(cu[r + 1])
+        q64[s1 - ne:s1] = O.widen_bf16(q_bits[s1 - ne:s1].cpu().numpy())
+    k64 = O.widen_bf16(inp["k"].view(torch.int16).cpu().numpy())
+    hid = inp["hidden"].view(torch.int16).cpu().numpy()
+    pos = inp["positions"].cpu().numpy()
+    with threadpool_limits(threads):
+        t0 = time.perf_counter()
+        out = O.run_chain(q64, k64, hid, pos, cu, w.n_query, w.block, w.top_p, w.sink, w.tail)
+        dt = time.perf_counter() - t0
+    try:
+        import multiprocessing
+        host_cores = multiprocessing.cpu_count()
+    except Exception:
+        host_cores = None
+    cpu = {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "seconds": round(dt, 2),
+           "sample": f"the full bench batch ({len(lens)} request(s), {T} tokens): fp64 numpy oracle "
+                     f"score+select+compact+history, BLAS limited to {threads} thread(s); "
+                     f"host reports {host_cores} logical CPUs"}
+
+    # full-size parity of this run (oracle fp64 pipeline vs the GPU chain)
+    gpu_ts = ws.token_scores[:T].double().cpu().numpy()
+    ref = out["token_scores"]
+    rel_err = np.abs(gpu_ts - ref) / np.abs(ref)
+    gpu_mask = ws.block_mask[:len(out["mask"])].cpu().numpy()
+    mism = int((gpu_mask.astype(bool) != out["mask"].astype(bool)).sum())
+    band = 0
+    if mism:
+        cub = O.block_offsets(cu, w.block)
+        for r, L in enumerate(lens):
+            bsl = slice(int(cub[r]), int(cub[r + 1]))
+            bd = O.band_blocks(out["block_scores"][bsl], L, w.block, w.top_p, w.sink, w.tail)
+            diff = np.flatnonzero(gpu_mask[bsl].astype(bool) != out["mask"][bsl].astype(bool))
+            band += int(bd[diff].sum())
+    same_mask = mism == 0
+    bit_exact = None
+    if same_mask:
+        n = int(out["cu_out"][-1])
+        got = ws.hidden_out[:n].view(torch.int16).cpu().numpy()
+        bit_exact = bool(np.array_equal(got, out["hidden_out"]) and
+                         np.array_equal(ws.positions_out[:n].cpu().numpy(), out["positions_out"]) and
+                         n == kept)
+    parity = {"max_rel_token_score_err": float(rel_err.max()),
+              "score_within_2e-3": bool((np.abs(gpu_ts - ref) <= 2e-3 * np.abs(ref) + 1e-12 * ref.sum()).all()),
+              "mask_mismatches": mism, "mask_mismatches_in_band": band,
+              "compaction_bit_exact": bit_exact}
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    main()

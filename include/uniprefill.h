@@ -1,0 +1,233 @@
+/*
+ * uniprefill.h — C ABI of the UniPrefill token-block pruning hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method source: the UniPrefill article page
+ * "中国科学院与腾讯微信合作解决AI排队等待问题" (CAS Institute of Automation, UCAS
+ * and Tencent WeChat; arXiv 2605.06221).  Section marks (§二, §三, Q&A 1)
+ * refer to that page.
+ *
+ * One pass of the path over a packed batch of B requests:
+ *   up_score        tail-query importance scores, per-token and per-block
+ *   up_select_topp  Top-p block mask with forced sink / tail blocks
+ *   up_compact      gather of the kept rows + positions, new cu_seqlens
+ *   up_drop_history append (layer id, kept tokens) to each request's ledger
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Packing.   Request r owns tokens cu_seqlens[r] .. cu_seqlens[r+1]-1 of a
+ *            packed token axis of length T = cu_seqlens[B]; cu_seqlens is
+ *            int32, non-decreasing, cu_seqlens[0] == 0.  Its blocks of
+ *            `block` (G) consecutive tokens are request-local, the last one
+ *            possibly shorter; block-indexed arrays are packed the same way
+ *            with cu_blocks[r+1]-cu_blocks[r] = ceil(L_r / G) (see
+ *            up_make_cu_blocks).  Most calls take both the host copy (`_h`,
+ *            used to validate and to size the launch) and the device copy
+ *            (`_d`, read by the kernels); the two must hold the same values.
+ * Memory.    Every buffer is owned by the caller.  Pointers named `_h` are
+ *            host memory; all others are device memory of the current HIP
+ *            device.  The library never allocates device memory and keeps no
+ *            pointer after a call returns (work still queued on the stream
+ *            aside).
+ * Streams.   Calls only enqueue work on `stream` (a hipStream_t; 0 is the
+ *            null stream) and never synchronise.  Results are valid once the
+ *            stream reaches them.  Calls that share a workspace or ledger
+ *            must not overlap.
+ * Layout.    Row-major with a contiguous last dimension; strides are in
+ *            elements unless the name says bytes.
+ * Errors.    Every entry point returns an up_status and never aborts.
+ *            Arguments are checked on the host before anything is enqueued;
+ *            on failure nothing is enqueued and up_last_error() (a
+ *            thread-local string) says why.  UP_ERR_HIP reports a launch
+ *            failure returned by the HIP runtime.
+ */
+#ifndef UNIPREFILL_H
+#define UNIPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UP_ABI_VERSION 1
+
+typedef enum up_status {
+  UP_OK = 0,
+  UP_ERR_INVALID = 1,     /* bad argument (null pointer, bad size, bad packing) */
+  UP_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement      */
+  UP_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace_size query */
+  UP_ERR_CAPACITY = 4,    /* output capacity smaller than the worst case       */
+  UP_ERR_HIP = 5          /* the HIP runtime reported an error                 */
+} up_status;
+
+/* ABI version of the loaded library (UP_ABI_VERSION of its build). */
+int up_abi_version(void);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* up_last_error(void);
+
+/* Static name of a status code. */
+const char* up_status_string(int status);
+
+/*
+ * Host helper: block offsets of a packed batch.
+ * cu_blocks_h[0] = 0, cu_blocks_h[r+1] = cu_blocks_h[r] + ceil(L_r / block).
+ * cu_seqlens_h: host int32 [num_seqs+1]; cu_blocks_h: host int32 [num_seqs+1]
+ * (written).  *num_blocks receives N = cu_blocks_h[num_seqs].
+ * Errors: UP_ERR_INVALID for null pointers, num_seqs < 0, block < 1 or
+ * non-monotone cu_seqlens_h.
+ */
+up_status up_make_cu_blocks(int num_seqs, const int32_t* cu_seqlens_h, int block,
+                            int32_t* cu_blocks_h, int64_t* num_blocks);
+
+/* ------------------------------------------------------------------------ */
+/* Steps 1-3: tail-query importance scores (§二 steps 1-2, §三)              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Workspace bytes up_score needs for this batch and shape.
+ */
+up_status up_score_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int hq, int hkv,
+                                  int head_dim, int n_query, size_t* bytes);
+
+/*
+ * up_score — importance estimation (§二 step 1: the last n tokens of each
+ * request query every key of the request; §三: scores, online normalisation,
+ * block aggregation) and block means (§二 step 2).
+ *
+ * For request r of length L, n_eff = min(n_query, L) tail rows
+ * i in [L-n_eff, L) (request-local), query head h and KV head
+ * g = h / (hq/hkv):
+ *     p[h,i,j] = exp(s[h,i,j]) / sum_{j' <= i} exp(s[h,i,j']),
+ *     s[h,i,j] = scale * <q[i,h,:], k[j,g,:]>        for keys j <= i,
+ *     token_scores[j] = sum_h sum_i p[h,i,j],
+ *     block_scores[b] = mean of token_scores over block b's tokens.
+ * So each request's token scores sum to hq * n_eff.
+ *
+ * q      bf16 [T, hq, head_dim]; element (t, h, c) at q[t*q_tok_stride +
+ *        h*q_head_stride + c].  Only the n_eff tail rows of each request are
+ *        read.  q and both strides must be 16-byte / 8-element aligned.
+ * k      bf16 [T, hkv, head_dim], same convention; every row is read.
+ * head_dim  64, 128 or 256.    hq % hkv == 0, 1 <= hq <= 1024.
+ * n_query   tail queries n, 1..4096.   block  G, a power of two in [16, 256].
+ * scale  softmax scale; 0 selects 1/sqrt(head_dim).
+ * token_scores  fp32 [T] or NULL.    block_scores  fp32 [N].
+ * cu_blocks_d   device int32 [B+1] from up_make_cu_blocks (same block).
+ * workspace     device, >= up_score_workspace_size bytes, 256-byte aligned.
+ * Deterministic: no floating-point atomics; repeated calls give identical
+ * bits.  Calling it on a subset of heads (q/k offset, local hq/hkv) gives
+ * partial scores whose sum over disjoint subsets is the full score, up to
+ * fp32 rounding (§三: per-device scores are summed before selection).
+ */
+up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                   const int32_t* cu_blocks_d,
+                   const void* q, int64_t q_tok_stride, int64_t q_head_stride, int hq,
+                   const void* k, int64_t k_tok_stride, int64_t k_head_stride, int hkv,
+                   int head_dim, int n_query, int block, float scale,
+                   float* token_scores, float* block_scores,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Step 4: Top-p block selection (§二 step 2, Q&A 1, §三 binary mask)         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * up_select_topp — for each request: blocks overlapping the first `sink` or
+ * the last `tail` tokens are forced; with total = sum of the request's block
+ * scores, the remaining blocks are added in (score desc, index asc) order
+ * while the kept mass (forced blocks included) is below top_p * total.
+ * The result is the smallest block set that contains the forced blocks and
+ * holds at least top_p of the mass.
+ *
+ * block_scores  fp32 [N], finite and >= 0.
+ * block_mask    uint8 [N] (written: 1 keep, 0 drop).
+ * kept_tokens   int32 [B] (written: tokens in kept blocks).
+ * top_p in (0, 1]; sink, tail >= 0; at most 16384 blocks per request.
+ * Sums run in fp64 in a fixed order (deterministic).
+ */
+up_status up_select_topp(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                         const int32_t* cu_blocks_d, const float* block_scores, int block,
+                         double top_p, int sink, int tail,
+                         uint8_t* block_mask, int32_t* kept_tokens, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Step 5: compaction (§二 step 3, §三 metadata update)                       */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes up_compact needs for this batch (tile status words). */
+up_status up_compact_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int block,
+                                    size_t* bytes);
+
+/*
+ * Prepare a compaction workspace once, before its first up_compact call
+ * (zeroes workspace_bytes bytes on `stream`).  Every up_compact call leaves
+ * the workspace in this state again when it completes, so one workspace
+ * serves any number of calls and any batch it is large enough for.
+ * workspace: 256-byte aligned, >= 256 bytes.
+ */
+up_status up_compact_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * up_compact — stream compaction of the kept blocks.  Kept tokens keep their
+ * order (request, then token); dropped rows are never read.  The input is
+ * not modified (the dropped rows stay in place, "frozen", §二 step 3).
+ *
+ * block_mask       uint8 [N] (nonzero = keep).
+ * hidden           [T rows], row t at hidden + t*row_stride_bytes, row_bytes
+ *                  bytes each; copied byte for byte (any dtype).
+ * positions        int32 [T] or NULL.
+ * hidden_out       [out_capacity_rows, row_bytes] contiguous (written).
+ * positions_out    int32 [out_capacity_rows] or NULL (written).
+ * cu_seqlens_out   int32 [B+1] (written): packing of the kept batch.
+ * out_capacity_rows must be >= T (the all-kept case), else UP_ERR_CAPACITY.
+ * workspace        >= up_compact_workspace_size bytes, 256-byte aligned,
+ *                  prepared by up_compact_workspace_init (and then only
+ *                  used by up_compact calls, one at a time).
+ * One kernel launch: a single-pass decoupled look-back scan (Merrill &
+ * Garland 2016) over tiles of blocks gives each tile its output offset
+ * (tiles are claimed in order from an atomic counter, so every look-back
+ * ends) and the tile copies its kept rows; the last tile to finish restores
+ * the workspace for the next call.
+ */
+up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                     const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                     const void* hidden, int64_t row_bytes, int64_t row_stride_bytes,
+                     const int32_t* positions,
+                     void* hidden_out, int32_t* positions_out, int32_t* cu_seqlens_out,
+                     int64_t out_capacity_rows, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Step 5 (cont.): drop-history ledger (§三)                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Ledger layout (int32 words, device memory):
+ *   [0] status bits (bit 0: an append found a request's record full)
+ *   [1] num_seqs   [2] capacity   [3] reserved
+ *   [4 + r]                          entries used by request r
+ *   [4 + B + 2*(r*capacity + e)]     entry e of request r: layer id
+ *   [4 + B + 2*(r*capacity + e) + 1]                       kept tokens
+ */
+size_t up_history_bytes(int num_seqs, int capacity);
+
+/* Clear a ledger (header written, all counts zero).  capacity >= 1. */
+up_status up_history_init(void* ledger, int num_seqs, int capacity, hipStream_t stream);
+
+/*
+ * up_drop_history — for every request r append (layer_id,
+ * cu_seqlens_out[r+1] - cu_seqlens_out[r]) to its record (§三: each drop
+ * records the layer and the number of kept tokens).  A full record keeps its
+ * entries, drops the new one and sets status bit 0.
+ */
+up_status up_drop_history(void* ledger, int num_seqs, int capacity, int layer_id,
+                          const int32_t* cu_seqlens_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UNIPREFILL_H */

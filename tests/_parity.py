@@ -1,0 +1,142 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and the
+oracle on the same seeded inputs, and compare them by the stated rules.
+
+Rules (from the required agreement of the pruning path):
+  scores       |gpu - ref| <= 2e-3 |ref| + 1e-12 * sum(ref)      (per token / block)
+  masks        identical except blocks whose cumulative mass interval meets
+               p +- 1e-4 (knife edge), counted and reported
+  compaction   bit-exact given the same mask
+  ledger       exact
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import token_block_sparsification_amd as U
+
+SCORE_RTOL = 2e-3
+BAND_EPS = 1e-4
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return O.widen_bf16(t.detach().cpu().contiguous().view(torch.int16).numpy())
+
+
+def check_scores(gpu: np.ndarray, ref: np.ndarray, cu, what="scores"):
+    """Per-element check with the floor scaled by each request's total."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 == s0:
+            continue
+        r, g = ref[s0:s1], gpu[s0:s1]
+        tol = SCORE_RTOL * np.abs(r) + 1e-12 * np.abs(r).sum()
+        bad = np.abs(g - r) > tol
+        if bad.any():
+            i = int(np.flatnonzero(bad)[0])
+            raise AssertionError(f"{what}: request {b}: {bad.sum()} of {s1 - s0} outside tolerance; "
+                                 f"first at {i}: gpu {g[i]!r} ref {r[i]!r}")
+    rel = np.abs(gpu - ref) / np.maximum(np.abs(ref), 1e-300)
+    return float(rel.max()) if rel.size else 0.0
+
+
+def check_mask(gpu_mask: np.ndarray, scores: np.ndarray, cu, G, p, sink, tail, ref_mask=None):
+    """Compare a GPU mask with the oracle's selection on `scores` (fp64).
+    Returns the number of mismatches (all of them inside the knife-edge band)."""
+    cub = O.block_offsets(cu, G)
+    if ref_mask is None:
+        ref_mask, _ = O.select_topp(scores, cu, G, p, sink, tail)
+    mism = 0
+    for b in range(len(cu) - 1):
+        L = int(cu[b + 1]) - int(cu[b])
+        sl = slice(int(cub[b]), int(cub[b + 1]))
+        diff = np.flatnonzero(gpu_mask[sl].astype(bool) != ref_mask[sl].astype(bool))
+        if len(diff) == 0:
+            continue
+        band = O.band_blocks(scores[sl], L, G, p, sink, tail, BAND_EPS)
+        outside = [int(i) for i in diff if not band[i]]
+        assert not outside, f"request {b}: mask differs outside the p band at blocks {outside[:10]}"
+        mism += len(diff)
+    return mism
+
+
+class GpuRun:
+    """Buffers + one pass of the path through the C ABI."""
+
+    def __init__(self, inputs, n_query, G, device="cuda", hidden=None, ledger_capacity=4):
+        self.dev = torch.device(device)
+        self.inp = inputs
+        self.G = G
+        self.n = n_query
+        self.batch = U.Batch.make(inputs["cu_seqlens"], G, self.dev)
+        self.q = inputs["q"].to(self.dev)
+        self.k = inputs["k"].to(self.dev)
+        h = inputs["hidden"] if hidden is None else hidden
+        self.hidden = h.to(self.dev)
+        self.positions = inputs["positions"].to(self.dev)
+        hq, d = self.q.shape[1], self.q.shape[2]
+        hkv = self.k.shape[1]
+        self.ws = U.Workspace.make(self.batch, hq, hkv, d, n_query, self.hidden, self.dev)
+        self.cap = ledger_capacity
+        self.ledger = torch.empty(U.up_history_bytes(self.batch.num_seqs, ledger_capacity) // 4,
+                                  dtype=torch.int32, device=self.dev)
+        U.up_history_init(self.ledger, self.batch.num_seqs, ledger_capacity)
+
+    def run(self, p=0.99, sink=128, tail=128, layer_id=0, scale=0.0):
+        U.run_chain(self.batch, self.ws, self.q, self.k, self.hidden, self.positions, self.ledger,
+                    self.cap, layer_id, n_query=self.n, top_p=p, sink=sink, tail=tail, scale=scale)
+        torch.cuda.synchronize()
+        ws = self.ws
+        T, N, B = self.batch.num_tokens, self.batch.num_blocks, self.batch.num_seqs
+        return dict(
+            token_scores=ws.token_scores[:T].double().cpu().numpy(),
+            block_scores=ws.block_scores[:N].cpu().numpy(),
+            mask=ws.block_mask[:N].cpu().numpy(),
+            kept=ws.kept_tokens[:B].cpu().numpy(),
+            cu_out=ws.cu_seqlens_out.cpu().numpy(),
+        )
+
+    def ledger_entries(self):
+        led = self.ledger.cpu().numpy()
+        B, cap = self.batch.num_seqs, self.cap
+        out = []
+        for r in range(B):
+            cnt = int(led[4 + r])
+            ent = led[4 + B + 2 * r * cap: 4 + B + 2 * (r * cap + cnt)].reshape(-1, 2)
+            out.append([(int(a), int(b)) for a, b in ent])
+        return int(led[0]), out
+
+
+def oracle_scores(inputs, n_query, G, scale=None):
+    q = bf16_to_f64(inputs["q"])
+    k = bf16_to_f64(inputs["k"])
+    cu = inputs["cu_seqlens"].numpy()
+    c = O.token_scores(q, k, cu, n_query, scale)
+    return c, O.block_scores(c, cu, G)
+
+
+def check_compaction(run: GpuRun, mask: np.ndarray, kept_gpu=None):
+    """Bit-exact compaction check given `mask`: the oracle picks the rows
+    (token_keep + flatnonzero); torch.index_select gathers the expected bytes."""
+    cu = run.batch.cu_seqlens_h.numpy()
+    keep = O.token_keep(mask, cu, run.G)
+    idx = torch.from_numpy(np.flatnonzero(keep)).to(run.dev)
+    n = int(idx.numel())
+    ws = run.ws
+    cu_out = ws.cu_seqlens_out.cpu().numpy()
+    exp_cu = [0]
+    for b in range(len(cu) - 1):
+        exp_cu.append(exp_cu[-1] + int(keep[cu[b]:cu[b + 1]].sum()))
+    assert list(cu_out) == exp_cu, (list(cu_out)[:8], exp_cu[:8])
+    hid = run.hidden.reshape(run.hidden.shape[0], -1)
+    exp_h = hid.index_select(0, idx).contiguous()
+    got_h = ws.hidden_out.reshape(ws.hidden_out.shape[0], -1)[:n].contiguous()
+    assert torch.equal(exp_h.view(torch.uint8), got_h.view(torch.uint8)), "hidden rows differ"
+    assert torch.equal(run.positions.index_select(0, idx), ws.positions_out[:n])
+    if kept_gpu is not None:
+        assert list(np.diff(cu_out)) == list(kept_gpu)
+    return n

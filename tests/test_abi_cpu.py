@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+headers declare, host helpers compute what the header says, and arguments
+that the host can reject are rejected with a status (never an abort)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch
+
+import token_block_sparsification_amd as U
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h, encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"\b(up_[a-z0-9_]+)\s*\(", src):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = U.lib()
+    declared = _declared_symbols()
+    assert {"up_score", "up_select_topp", "up_compact", "up_drop_history"} <= declared
+    missing = [n for n in sorted(declared) if not hasattr(lib, n)]
+    assert not missing, missing
+    assert U.up_abi_version() == 1
+
+
+def test_binding_covers_every_declared_symbol():
+    declared = _declared_symbols()
+    assert declared <= set(U._SIGNATURES), declared - set(U._SIGNATURES)
+
+
+def test_make_cu_blocks():
+    cb, n = U.up_make_cu_blocks([0, 10, 10, 75, 203], 32)
+    assert cb.tolist() == [0, 1, 1, 4, 8] and n == 8
+    with pytest.raises(U.UniprefillError) as e:
+        U.up_make_cu_blocks([0, 10, 5], 32)
+    assert e.value.status == 1 and "decreases" in str(e.value)
+
+
+def test_workspace_sizes():
+    cu = [0, 131072]
+    ws = U.up_score_workspace_size(cu, 32, 8, 128, 128)
+    # partials + biases + per-(KV head, row group) column partials
+    assert ws >= 8 * 131072 * 4
+    assert U.up_compact_workspace_size(cu, 64) >= 2048 * 8
+    assert U.up_history_bytes(3, 5) == 4 * (4 + 3 + 2 * 3 * 5)
+
+
+def _score_status(**over):
+    lib = U.lib()
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    args = dict(num_seqs=1, cu_h=cu.data_ptr(), cu_d=16, cb_d=16, q=4096, q_tok=64, q_head=16,
+                hq=4, k=8192, k_tok=32, k_head=16, hkv=2, d=64, n=128, G=64, scale=0.0,
+                ts=None, bs=16, ws=256, ws_bytes=1 << 30)
+    args.update(over)
+    st = lib.up_score(args["num_seqs"], args["cu_h"], args["cu_d"], args["cb_d"], args["q"],
+                      args["q_tok"], args["q_head"], args["hq"], args["k"], args["k_tok"],
+                      args["k_head"], args["hkv"], args["d"], args["n"], args["G"], args["scale"],
+                      args["ts"], args["bs"], args["ws"], args["ws_bytes"], None)
+    return st, U.up_last_error()
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(d=96), 2, "head_dim"),
+    (dict(hq=6, hkv=4), 1, "hq"),
+    (dict(n=0), 2, "n_query"),
+    (dict(G=48), 2, "power of two"),
+    (dict(G=512), 2, "power of two"),
+    (dict(scale=-1.0), 1, "scale"),
+    (dict(q=4098), 2, "aligned"),
+    (dict(q_tok=60), 2, "aligned"),
+    (dict(ws_bytes=16), 3, "workspace"),
+    (dict(bs=None), 1, "NULL"),
+    (dict(ws=300), 1, "256-byte"),
+])
+def test_score_rejects_bad_arguments(over, status, msg):
+    st, err = _score_status(**over)
+    assert st == status and msg in err, (st, err)
+
+
+def test_score_rejects_bad_packing():
+    bad = torch.tensor([0, 100, 50], dtype=torch.int32)
+    st, err = _score_status(num_seqs=2, cu_h=bad.data_ptr())
+    assert st == 1 and "decreases" in err
+    nz = torch.tensor([5, 100], dtype=torch.int32)
+    st, err = _score_status(cu_h=nz.data_ptr())
+    assert st == 1 and "[0]" in err
+
+
+def test_select_rejects_bad_arguments():
+    lib = U.lib()
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    for p, sink, tail, msg in [(0.0, 128, 128, "top_p"), (1.5, 128, 128, "top_p"),
+                               (0.9, -1, 128, "sink")]:
+        st = lib.up_select_topp(1, cu.data_ptr(), 16, 16, 16, 64, p, sink, tail, 16, 16, None)
+        assert st == 1 and msg in U.up_last_error()
+    big = torch.tensor([0, 64 * 16385], dtype=torch.int32)
+    st = lib.up_select_topp(1, big.data_ptr(), 16, 16, 16, 64, 0.99, 128, 128, 16, 16, None)
+    assert st == 2 and "blocks" in U.up_last_error()
+
+
+def test_compact_rejects_bad_arguments():
+    lib = U.lib()
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    base = [1, cu.data_ptr(), 16, 16, 64, 16, 4096, 512, 512, 4096, 8192, 8192, 16, 256, 256,
+            1 << 20, None]
+    cases = [((13, 255), 4, "capacity"), ((8, 256), 1, "row_stride"), ((7, 0), 1, "row_bytes"),
+             ((15, 16), 3, "workspace"), ((9, None), 1, "positions"), ((14, 300), 1, "256-byte")]
+    for (i, v), status, msg in cases:
+        a = list(base)
+        a[i] = v
+        st = lib.up_compact(*a)
+        assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())
+
+
+def test_history_rejects_bad_arguments():
+    lib = U.lib()
+    assert lib.up_history_init(None, 2, 4, None) == 1
+    assert lib.up_history_init(16, 2, 0, None) == 1
+    assert lib.up_drop_history(16, 2, 4, 0, None, None) == 1
+    assert lib.up_history_bytes(-1, 4) == 0

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every test runs on seeded synthetic inputs from workloads/ and compares by the
+rules in _parity.py.  Sizes span several MFMA tiles, key chunks, LDS sort
+sizes and compaction tiles, with ragged tails, requests shorter than n, empty
+requests and partial last blocks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import token_block_sparsification_amd as U
+import workloads as W
+from _parity import (GpuRun, bf16_to_f64, check_compaction, check_mask, check_scores,
+                     oracle_scores)
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, **kv):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kv.items()), flush=True)
+
+
+def _end_to_end(inputs, n, G, p=0.99, sink=128, tail=128, layer_id=3, name=""):
+    run = GpuRun(inputs, n, G)
+    out = run.run(p=p, sink=sink, tail=tail, layer_id=layer_id)
+    cu = inputs["cu_seqlens"].numpy()
+    c_ref, b_ref = oracle_scores(inputs, n, G)
+    r1 = check_scores(out["token_scores"], c_ref, cu, "token scores")
+    cub = O.block_offsets(cu, G)
+    r2 = check_scores(out["block_scores"], b_ref, cub, "block scores")
+    # isolated select: oracle on the GPU's own fp32 block scores
+    m_iso = check_mask(out["mask"], out["block_scores"].astype(np.float64), cu, G, p, sink, tail)
+    # end to end: oracle's fp64 pipeline
+    m_e2e = check_mask(out["mask"], b_ref, cu, G, p, sink, tail)
+    _, kept_ref = O.select_topp(out["block_scores"].astype(np.float64), cu, G, p, sink, tail)
+    assert list(out["kept"]) == list(kept_ref)
+    n_rows = check_compaction(run, out["mask"], out["kept"])
+    status, entries = run.ledger_entries()
+    ref_led = O.history_new(len(cu) - 1)
+    O.history_append(ref_led, layer_id, out["cu_out"])
+    assert status == 0 and entries == ref_led
+    _report(name, T=int(cu[-1]), max_rel_token=f"{r1:.2e}", max_rel_block=f"{r2:.2e}",
+            mask_mismatch_iso=m_iso, mask_mismatch_e2e=m_e2e, kept_rows=n_rows)
+    return run, out
+
+
+def test_small_workload():
+    w = W.get_workload("small_L2048")
+    _end_to_end(W.make_inputs(w), w.n_query, w.block, name=w.name)
+
+
+RAGGED = [0, 1, 63, 64, 65, 127, 128, 129, 300, 0, 1000, 2500, 4097]
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 4, 4), (128, 8, 2), (256, 8, 1), (128, 32, 8)])
+def test_ragged_batch(d, hq, hkv):
+    w = W.Workload(name=f"ragged_d{d}", lengths=tuple(RAGGED), hq=hq, hkv=hkv, head_dim=d,
+                   hidden_dim=96, hidden_dtype="bf16", seed=4000 + d + hq, plant_frac=0.05,
+                   num_seqs=len(RAGGED))
+    _end_to_end(W.make_inputs(w), 128, 64, name=w.name)
+
+
+@pytest.mark.parametrize("n,G", [(32, 32), (512, 128), (200, 16), (1, 256), (128, 64)])
+def test_n_and_block_sweep(n, G):
+    w = W.Workload(name=f"sweep_n{n}_G{G}", lengths=(3000, 777, 5000), hq=16, hkv=2, head_dim=256,
+                   hidden_dim=64, hidden_dtype="f32", seed=5000 + n + G, plant_frac=0.02,
+                   n_query=n, block=G, num_seqs=3)
+    _end_to_end(W.make_inputs(w), n, G, name=w.name)
+
+
+def test_tail_equals_n_and_small_p():
+    w = W.Workload(name="p_sweep", lengths=(4096, 2000), hq=8, hkv=2, head_dim=128, hidden_dim=32,
+                   hidden_dtype="bf16", seed=6001, plant_frac=0.1, num_seqs=2)
+    inputs = W.make_inputs(w)
+    for p, sink, tail in [(0.5, 128, 128), (0.9, 0, 0), (1.0, 64, 256), (0.95, 128, 32)]:
+        _end_to_end(inputs, 32, 64, p=p, sink=sink, tail=tail, name=f"p{p}_s{sink}_t{tail}")
+
+
+def test_explicit_scale():
+    w = W.Workload(name="scale", lengths=(1500,), hq=4, hkv=2, head_dim=64, hidden_dim=16,
+                   hidden_dtype="f32", seed=6100, plant_count=2)
+    inputs = W.make_inputs(w)
+    run = GpuRun(inputs, 128, 64)
+    out = run.run(scale=0.3)
+    c_ref, _ = oracle_scores(inputs, 128, 64, scale=0.3)
+    check_scores(out["token_scores"], c_ref, inputs["cu_seqlens"].numpy())
+
+
+def test_rows_sum_and_nan_rows_unread():
+    """Each request's token scores sum to Hq * n_eff; the non-tail Q rows are
+    NaN in every generated input, so any read of them would poison scores."""
+    w = W.Workload(name="sums", lengths=(50, 5000, 129), hq=8, hkv=4, head_dim=128, hidden_dim=8,
+                   hidden_dtype="f32", seed=6200, num_seqs=3)
+    inputs = W.make_inputs(w)
+    assert torch.isnan(inputs["q"][50].float()).all()      # first row of request 1 (not a tail row)
+    out = GpuRun(inputs, 128, 64).run()
+    cu = inputs["cu_seqlens"].numpy()
+    for b, L in enumerate(w.lengths):
+        s = out["token_scores"][cu[b]:cu[b + 1]].sum()
+        assert abs(s - 8 * min(128, L)) < 1e-4 * 8 * 128, (b, s)
+
+
+def test_head_split_additivity():
+    """Scores of disjoint head subsets (sliced q/k views) add up to the full
+    scores (the per-device local scores of a head-parallel layer)."""
+    w = W.Workload(name="split", lengths=(3000, 1200), hq=8, hkv=4, head_dim=128, hidden_dim=8,
+                   hidden_dtype="f32", seed=6300, plant_frac=0.05, num_seqs=2)
+    inputs = W.make_inputs(w)
+    dev = torch.device("cuda")
+    q, k = inputs["q"].to(dev), inputs["k"].to(dev)
+    batch = U.Batch.make(inputs["cu_seqlens"], 64, dev)
+    T, N = batch.num_tokens, batch.num_blocks
+
+    def score(qs, ks):
+        ws = torch.empty(U.up_score_workspace_size(batch.cu_seqlens_h, qs.shape[1], ks.shape[1], 128,
+                                                   128), dtype=torch.uint8, device=dev)
+        ts = torch.empty(T, device=dev)
+        bs = torch.empty(N, device=dev)
+        U.up_score(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, qs, ks, 128, 64, 0.0,
+                   ts, bs, ws)
+        return ts.double()
+
+    full = score(q, k)
+    parts = score(q[:, 0:2], k[:, 0:1]) + score(q[:, 2:8], k[:, 1:4])
+    torch.cuda.synchronize()
+    rel = ((parts - full).abs() / full.abs()).max().item()
+    assert rel < 1e-5, rel
+
+
+def test_select_isolated():
+    """Selection alone on given fp32 scores (incl. exact ties, one-hot, zeros
+    and up to 16384 blocks per request): masks and kept counts must equal the
+    oracle's on the same values (fp32 sums are exact in fp64 at these ranges)."""
+    dev = torch.device("cuda")
+    G = 16
+    lens = [0, 5, 16 * 16384, 16 * 3000 - 7, 16 * 1000, 16 * 40, 16 * 40, 16 * 40]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    batch = U.Batch.make(torch.from_numpy(cu), G, dev)
+    cub = batch.cu_blocks_h.numpy()
+    sc = W.gen.make_scores(77, batch.num_blocks).numpy()
+    # request 5: all equal (ties); request 6: one-hot; request 7: all zero
+    sc[cub[5]:cub[6]] = 1.5
+    sc[cub[6]:cub[7]] = 0.0
+    sc[cub[6] + 17] = 3.0
+    sc[cub[7]:cub[8]] = 0.0
+    for p, sink, tail in [(0.99, 128, 128), (0.5, 0, 16), (1.0, 32, 32), (0.9, 0, 0)]:
+        bs = torch.from_numpy(sc).to(dev)
+        mask = torch.empty(batch.num_blocks, dtype=torch.uint8, device=dev)
+        kept = torch.empty(len(lens), dtype=torch.int32, device=dev)
+        U.up_select_topp(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, bs, G, p, sink,
+                         tail, mask, kept)
+        torch.cuda.synchronize()
+        ref_m, ref_k = O.select_topp(sc.astype(np.float64), cu, G, p, sink, tail)
+        assert np.array_equal(mask.cpu().numpy(), ref_m), p
+        assert list(kept.cpu().numpy()) == list(ref_k)
+
+
+@pytest.mark.parametrize("dtype,dim,strided", [
+    (torch.bfloat16, 4096, False), (torch.float32, 512, False), (torch.bfloat16, 96, True),
+    (torch.uint8, 6, False), (torch.float16, 3, True), (torch.int32, 5, False)])
+def test_compact_isolated(dtype, dim, strided):
+    """Compaction alone on random masks, any dtype and row size (16/8/4/1-byte
+    vector paths), packed or strided rows, positions with gaps."""
+    dev = torch.device("cuda")
+    lens = [0, 3, 64, 65, 1000, 0, 2049, 130]
+    G = 32
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    batch = U.Batch.make(cu, G, dev)
+    T = batch.num_tokens
+    gen = torch.Generator().manual_seed(dim)
+    base = torch.randint(-100, 100, (T, dim + (7 if strided else 0)), generator=gen)
+    hidden = base.to(dtype).to(dev)
+    if strided:
+        hidden = hidden[:, :dim]
+    pos = (torch.arange(T, dtype=torch.int32) * 3 + 11).to(dev)
+    for frac in (0.0, 0.4, 1.0):
+        mask_np = (torch.rand(batch.num_blocks, generator=gen) < frac).numpy().astype(np.uint8)
+        mask = torch.from_numpy(mask_np).to(dev)
+        if frac == 0.0:   # one workspace serves every call: each call leaves it clean
+            ws = U.new_compact_workspace(batch.cu_seqlens_h, G, dev)
+        out = torch.full((T + 5, dim), 0, dtype=dtype, device=dev)
+        pout = torch.full((T + 5,), -1, dtype=torch.int32, device=dev)
+        cu_out = torch.empty(len(lens) + 1, dtype=torch.int32, device=dev)
+        U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, hidden,
+                     pos, out, pout, cu_out, ws)
+        torch.cuda.synchronize()
+        keep = O.token_keep(mask_np, cu.numpy(), G)
+        idx = torch.from_numpy(np.flatnonzero(keep)).to(dev)
+        n = idx.numel()
+        assert torch.equal(out[:n], hidden.index_select(0, idx))
+        assert torch.equal(pout[:n], pos.index_select(0, idx))
+        assert (pout[n:] == -1).all() and (out[n:] == 0).all()   # nothing past the kept rows
+        _, _, cu_ref = O.compact(mask_np, np.zeros((T, 1)), np.zeros(T), cu.numpy(), G)
+        assert list(cu_out.cpu().numpy()) == list(cu_ref)
+        assert not ws.view(torch.int32)[:2].any() and not ws[256:].any()   # left clean
+
+
+def test_compact_all_empty_and_no_positions():
+    dev = torch.device("cuda")
+    cu = torch.tensor([0, 0, 0, 0], dtype=torch.int32)
+    batch = U.Batch.make(cu, 64, dev)
+    ws = U.new_compact_workspace(cu, 64, dev)
+    cu_out = torch.full((4,), 99, dtype=torch.int32, device=dev)
+    h = torch.zeros((1, 8), device=dev)
+    U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, 64,
+                 torch.zeros(1, dtype=torch.uint8, device=dev), h, None, torch.zeros((1, 8), device=dev),
+                 None, cu_out, ws)
+    torch.cuda.synchronize()
+    assert cu_out.tolist() == [0, 0, 0, 0]
+
+
+def test_history_appends_and_overflow():
+    dev = torch.device("cuda")
+    B, cap = 3, 2
+    led = torch.empty(U.up_history_bytes(B, cap) // 4, dtype=torch.int32, device=dev)
+    U.up_history_init(led, B, cap)
+    ref = O.history_new(B)
+    for layer, cu in [(3, [0, 10, 10, 25]), (7, [0, 4, 4, 20])]:
+        U.up_drop_history(led, B, cap, layer, torch.tensor(cu, dtype=torch.int32, device=dev))
+        O.history_append(ref, layer, cu)
+    torch.cuda.synchronize()
+    l = led.cpu().numpy()
+    assert l[0] == 0 and list(l[1:3]) == [B, cap] and list(l[4:4 + B]) == [2, 2, 2]
+    got = [[tuple(l[4 + B + 2 * (r * cap + e): 4 + B + 2 * (r * cap + e) + 2]) for e in range(2)]
+           for r in range(B)]
+    assert got == [[tuple(x) for x in row] for row in ref]
+    U.up_drop_history(led, B, cap, 9, torch.tensor([0, 1, 2, 3], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    l2 = led.cpu().numpy()
+    assert l2[0] & 1 and np.array_equal(l2[4:], l[4:])   # full records keep their entries
+    U.up_drop_history(led, 2, cap, 9, torch.tensor([0, 1, 2], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert led.cpu().numpy()[0] & 2                      # shape mismatch flagged, nothing written
+
+
+def test_determinism():
+    w = W.Workload(name="det", lengths=(20000, 3000), hq=32, hkv=8, head_dim=128, hidden_dim=256,
+                   hidden_dtype="bf16", seed=6400, plant_frac=0.05, num_seqs=2)
+    run = GpuRun(W.make_inputs(w), 128, 64)
+    first = run.run()
+    n = int(first["cu_out"][-1])
+    h0 = run.ws.hidden_out[:n].view(torch.int16).clone()
+    for _ in range(5):
+        again = run.run()
+        for key in ("token_scores", "block_scores", "mask", "kept", "cu_out"):
+            assert np.array_equal(first[key], again[key]), key
+        assert torch.equal(h0, run.ws.hidden_out[:n].view(torch.int16))

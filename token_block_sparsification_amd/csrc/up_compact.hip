@@ -1,0 +1,419 @@
+// Step 5 of the pruning path: stream compaction and the drop-history ledger.
+//
+// Method (UniPrefill page "中国科学院与腾讯微信合作解决AI排队等待问题", §二 step 3 and
+// §三): tokens of dropped blocks are skipped by every later layer, so the
+// kept rows (hidden states and positions) are gathered into a packed batch
+// with updated per-request lengths, and each drop appends (layer id, kept
+// tokens) to the request's drop-history ledger.
+//
+// up_compact is one kernel: a single-pass decoupled look-back scan (Merrill & Garland, "Single-pass Parallel Prefix
+// Scan with Decoupled Look-back", 2016) over tiles of whole blocks.  Each
+// workgroup claims the next tile from an atomic ticket (so every tile it may
+// wait on has already started), publishes its kept-token count, walks back
+// over its predecessors' published counts to get its output offset, publishes
+// the inclusive count, and copies its kept blocks.  Because the mask is per
+// block, a kept block is a run of G consecutive rows, copied as one flat
+// byte range with wide vector loads and stores; dropped rows are never read.
+// The last workgroup to finish (a done counter) clears the tile status words
+// and both counters, so the next call starts from a clean workspace without
+// a separate clearing launch; up_compact_workspace_init prepares a new one.
+#include "up_internal.h"
+
+namespace up {
+namespace {
+
+constexpr int kCompactThreads = 256;
+constexpr int kMaxTileBlocks = 64;
+constexpr uint64_t kFlagAgg = 1ull << 62;
+constexpr uint64_t kFlagIncl = 2ull << 62;
+constexpr uint64_t kValueMask = (1ull << 62) - 1;
+constexpr int kSpinLimit = 1 << 24;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+struct CompactArgs {
+  const int32_t* cu_seqlens;
+  const int32_t* cu_blocks;
+  const uint8_t* mask;
+  const char* hidden;
+  const int32_t* positions;
+  char* hidden_out;
+  int32_t* positions_out;
+  int32_t* cu_out;
+  uint64_t* flags;    // [num_tiles] tile status words
+  uint32_t* ctl;      // [0] tile ticket, [1] done counter, [2] sticky look-back timeout flag
+  int64_t row_bytes, row_stride, capacity, num_blocks, num_tiles;
+  int num_seqs, block, tile_blocks;
+};
+
+// Zero a whole compaction workspace (control words and tile status words).
+__global__ void up_compact_init_kernel(uint32_t* ws, int64_t nwords) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nwords) ws[i] = 0;
+}
+
+template <int VW> struct Vec;
+template <> struct Vec<16> { typedef u32x4_t T; };
+template <> struct Vec<8> { typedef u32x2_t T; };
+template <> struct Vec<4> { typedef uint32_t T; };
+template <> struct Vec<1> { typedef uint8_t T; };
+
+// Copy nbytes (a multiple of VW) from src to dst, whole workgroup.
+template <int VW>
+__device__ __forceinline__ void copy_flat(char* __restrict__ dst, const char* __restrict__ src,
+                                          int64_t nbytes) {
+  typedef typename Vec<VW>::T V;
+  constexpr int U = 4;
+  const V* s = reinterpret_cast<const V*>(src);
+  V* d = reinterpret_cast<V*>(dst);
+  const int64_t n = nbytes / VW;
+  int64_t i = threadIdx.x;
+  for (; i + (U - 1) * kCompactThreads < n; i += U * kCompactThreads) {
+    V r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = __builtin_nontemporal_load(s + i + u * kCompactThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(r[u], d + i + u * kCompactThreads);
+  }
+  for (; i < n; i += kCompactThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
+}
+
+// Copy `rows` rows of row_bytes from a strided source to a packed destination
+// (one wave per row; not the hot path: the packed case goes through copy_flat).
+template <int VW>
+__device__ __forceinline__ void copy_rows(char* __restrict__ dst, const char* __restrict__ src,
+                                          int rows, int64_t row_bytes, int64_t row_stride) {
+  typedef typename Vec<VW>::T V;
+  const int64_t vpr = row_bytes / VW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = wave; r < rows; r += kCompactThreads / 64) {
+    const V* s = reinterpret_cast<const V*>(src + (int64_t)r * row_stride);
+    V* d = reinterpret_cast<V*>(dst + (int64_t)r * row_bytes);
+    for (int64_t c = lane; c < vpr; c += 64) __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
+  }
+}
+
+template <int VW>
+__global__ void __launch_bounds__(kCompactThreads) up_compact_kernel(CompactArgs a) {
+  __shared__ int64_t s_tile;
+  __shared__ int64_t s_excl;
+  __shared__ int s_last;
+  __shared__ int s_src[kMaxTileBlocks];     // first source token of each block
+  __shared__ int s_size[kMaxTileBlocks];    // rows of each block if kept, else 0
+  __shared__ int64_t s_dst[kMaxTileBlocks]; // in-tile exclusive prefix of kept rows
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_tile = (int64_t)atomicAdd(&a.ctl[0], 1u);
+  __syncthreads();
+  const int64_t t = s_tile;
+
+  if (t == 0 && tid == 0) {
+    // Output packing starts at 0; requests with no blocks before the first
+    // block end at 0 as well.
+    a.cu_out[0] = 0;
+    for (int r = 0; r < a.num_seqs && a.cu_blocks[r + 1] == 0; ++r) a.cu_out[r + 1] = 0;
+  }
+
+  if (t < a.num_tiles) {
+    const int64_t b0 = t * a.tile_blocks;
+    const int nblk = (int)min((int64_t)a.tile_blocks, a.num_blocks - b0);
+
+    if (wave == 0) {
+      int64_t ksize = 0;
+      int req = 0, lb = 0;
+      if (lane < nblk) {
+        const int64_t b = b0 + lane;
+        int lo = 0, hi = a.num_seqs;  // cu_blocks[lo] <= b < cu_blocks[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
+        }
+        req = lo;
+        const int s0 = a.cu_seqlens[req];
+        const int L = a.cu_seqlens[req + 1] - s0;
+        lb = (int)(b - a.cu_blocks[req]);
+        const int size = min(lb * a.block + a.block, L) - lb * a.block;
+        ksize = a.mask[b] ? size : 0;
+        s_src[lane] = s0 + lb * a.block;
+        s_size[lane] = (int)ksize;
+      }
+      // inclusive scan of kept rows across the tile's blocks
+      int64_t incl = ksize;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const int64_t agg = __shfl(incl, 63);
+      if (lane < nblk) s_dst[lane] = incl - ksize;
+
+      int64_t excl = 0;
+      if (lane == 0) {
+        if (t == 0) {
+          __hip_atomic_store(&a.flags[0], kFlagIncl | (uint64_t)agg, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          __hip_atomic_store(&a.flags[t], kFlagAgg | (uint64_t)agg, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          int64_t p = t - 1;
+          while (p >= 0) {
+            uint64_t f = 0;
+            int spins = 0;
+            for (;;) {
+              f = __hip_atomic_load(&a.flags[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+              if ((f >> 62) != 0 || ++spins >= kSpinLimit) break;
+              __builtin_amdgcn_s_sleep(1);
+            }
+            if ((f >> 62) == 0) {  // predecessor never published: give up, flag it
+              atomicOr(&a.ctl[2], 1u);
+              break;
+            }
+            excl += (int64_t)(f & kValueMask);
+            if ((f >> 62) == 2) break;
+            --p;
+          }
+          __hip_atomic_store(&a.flags[t], kFlagIncl | (uint64_t)(excl + agg), __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+        s_excl = excl;
+      }
+      excl = __shfl(excl, 0);
+
+      // Requests whose last block is in this tile (and empty requests right
+      // after them) end at this block's inclusive count.
+      if (lane < nblk) {
+        const int nb_r = a.cu_blocks[req + 1] - a.cu_blocks[req];
+        if (lb == nb_r - 1) {
+          const int32_t end = (int32_t)(excl + incl);
+          a.cu_out[req + 1] = end;
+          const int32_t bend = a.cu_blocks[req + 1];
+          for (int r2 = req + 1; r2 < a.num_seqs && a.cu_blocks[r2 + 1] == bend; ++r2)
+            a.cu_out[r2 + 1] = end;
+        }
+      }
+    }
+    __syncthreads();
+
+    const int64_t excl = s_excl;
+    for (int i = 0; i < nblk; ++i) {
+      const int rows = s_size[i];
+      if (rows == 0) continue;
+      const int64_t dst_row = excl + s_dst[i];
+      if (dst_row + rows > a.capacity) continue;  // never write past the output
+      const int64_t src_row = s_src[i];
+      if (a.row_stride == a.row_bytes)
+        copy_flat<VW>(a.hidden_out + dst_row * a.row_bytes, a.hidden + src_row * a.row_bytes,
+                      (int64_t)rows * a.row_bytes);
+      else
+        copy_rows<VW>(a.hidden_out + dst_row * a.row_bytes, a.hidden + src_row * a.row_stride, rows,
+                      a.row_bytes, a.row_stride);
+      if (a.positions)
+        for (int i2 = tid; i2 < rows; i2 += kCompactThreads)
+          a.positions_out[dst_row + i2] = a.positions[src_row + i2];
+    }
+  }
+
+  // Done counter: the last workgroup leaves the status words and counters
+  // zeroed for the next call (every other workgroup has finished its
+  // look-back before it counted itself done).
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ctl[1], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == gridDim.x - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (s_last) {
+    for (int64_t i = tid; i < a.num_tiles; i += kCompactThreads) a.flags[i] = 0;
+    if (tid == 0) {
+      a.ctl[0] = 0;
+      a.ctl[1] = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Drop-history ledger.
+// ---------------------------------------------------------------------------
+constexpr int kLedgerHeader = 4;
+
+__global__ void up_history_init_kernel(int32_t* led, int num_seqs, int capacity) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) {
+    led[0] = 0;
+    led[1] = num_seqs;
+    led[2] = capacity;
+    led[3] = 0;
+  }
+  if (i < num_seqs) led[kLedgerHeader + i] = 0;
+}
+
+__global__ void up_history_append_kernel(int32_t* led, int num_seqs, int capacity, int layer,
+                                         const int32_t* cu_out) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= num_seqs) return;
+  if (led[1] != num_seqs || led[2] != capacity) {  // ledger set up for another shape
+    if (r == 0) atomicOr(&led[0], 2);
+    return;
+  }
+  const int cnt = led[kLedgerHeader + r];
+  const int kept = cu_out[r + 1] - cu_out[r];
+  if (cnt < capacity) {
+    int32_t* e = led + kLedgerHeader + num_seqs + 2 * ((int64_t)r * capacity + cnt);
+    e[0] = layer;
+    e[1] = kept;
+    led[kLedgerHeader + r] = cnt + 1;
+  } else {
+    atomicOr(&led[0], 1);
+  }
+}
+
+}  // namespace
+
+int compact_tile_blocks(int block) {
+  int tb = 64 / block;
+  return tb < 1 ? 1 : tb;
+}
+
+}  // namespace up
+
+namespace {
+
+int64_t compact_tiles(int num_seqs, const int32_t* cu_h, int block) {
+  int64_t N = 0;
+  for (int r = 0; r < num_seqs; ++r) N += up::ceil_div(cu_h[r + 1] - cu_h[r], block);
+  return up::ceil_div(N, up::compact_tile_blocks(block));
+}
+
+}  // namespace
+
+extern "C" {
+
+up_status up_compact_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int block,
+                                    size_t* bytes) {
+  up::clear_error();
+  if (!bytes) return up::set_error(UP_ERR_INVALID, "bytes is NULL");
+  if (block < 1) return up::set_error(UP_ERR_INVALID, "block < 1");
+  int64_t T;
+  int mx;
+  up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &mx);
+  if (st != UP_OK) return st;
+  const int64_t tiles = compact_tiles(num_seqs, cu_seqlens_h, block);
+  *bytes = up::align_up(256 + (size_t)tiles * sizeof(uint64_t), 256);
+  return UP_OK;
+}
+
+up_status up_compact_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  up::clear_error();
+  if (!workspace) return up::set_error(UP_ERR_INVALID, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return up::set_error(UP_ERR_INVALID, "workspace not 256-byte aligned");
+  if (workspace_bytes < 256) return up::set_error(UP_ERR_WORKSPACE, "workspace smaller than 256 bytes");
+  up_status st = up::check_device();
+  if (st != UP_OK) return st;
+  const int64_t nwords = (int64_t)(workspace_bytes / 4);
+  hipLaunchKernelGGL(up::up_compact_init_kernel, dim3((unsigned)up::ceil_div(nwords, 256)), dim3(256),
+                     0, stream, static_cast<uint32_t*>(workspace), nwords);
+  return up::check_launch("up_compact_init_kernel");
+}
+
+up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                     const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                     const void* hidden, int64_t row_bytes, int64_t row_stride_bytes,
+                     const int32_t* positions, void* hidden_out, int32_t* positions_out,
+                     int32_t* cu_seqlens_out, int64_t out_capacity_rows, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  up::clear_error();
+  int64_t T;
+  int max_len;
+  up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &max_len);
+  if (st != UP_OK) return st;
+  if (block < 1 || block > 4096) return up::set_error(UP_ERR_INVALID, "block not in [1, 4096]");
+  if (row_bytes < 1 || row_stride_bytes < row_bytes)
+    return up::set_error(UP_ERR_INVALID, "need row_bytes >= 1 and row_stride_bytes >= row_bytes");
+  if (row_bytes > ((int64_t)1 << 30))
+    return up::set_error(UP_ERR_UNSUPPORTED, "row_bytes above 1 GiB");
+  if (out_capacity_rows < T)
+    return up::set_error(UP_ERR_CAPACITY, "out_capacity_rows %lld < T %lld",
+                         (long long)out_capacity_rows, (long long)T);
+  if (!cu_seqlens_d || !cu_blocks_d || !cu_seqlens_out || !workspace ||
+      (T > 0 && (!block_mask || !hidden || !hidden_out)))
+    return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if ((positions == nullptr) != (positions_out == nullptr))
+    return up::set_error(UP_ERR_INVALID, "positions and positions_out must both be set or both NULL");
+  if ((uintptr_t)workspace & 255) return up::set_error(UP_ERR_INVALID, "workspace not 256-byte aligned");
+  size_t need;
+  up_compact_workspace_size(num_seqs, cu_seqlens_h, block, &need);
+  if (workspace_bytes < need)
+    return up::set_error(UP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (num_seqs == 0) return UP_OK;
+  st = up::check_device();
+  if (st != UP_OK) return st;
+
+  up::CompactArgs a{};
+  a.cu_seqlens = cu_seqlens_d;
+  a.cu_blocks = cu_blocks_d;
+  a.mask = block_mask;
+  a.hidden = static_cast<const char*>(hidden);
+  a.positions = positions;
+  a.hidden_out = static_cast<char*>(hidden_out);
+  a.positions_out = positions_out;
+  a.cu_out = cu_seqlens_out;
+  a.ctl = static_cast<uint32_t*>(workspace);
+  a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + 256);
+  a.row_bytes = row_bytes;
+  a.row_stride = row_stride_bytes;
+  a.capacity = out_capacity_rows;
+  a.num_seqs = num_seqs;
+  a.block = block;
+  a.tile_blocks = up::compact_tile_blocks(block);
+  int64_t N = 0;
+  for (int r = 0; r < num_seqs; ++r) N += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], block);
+  a.num_blocks = N;
+  a.num_tiles = up::ceil_div(N, a.tile_blocks);
+
+  const uintptr_t al = (uintptr_t)hidden | (uintptr_t)hidden_out | (uintptr_t)row_bytes |
+                       (uintptr_t)row_stride_bytes;
+  const dim3 grid((unsigned)(a.num_tiles > 0 ? a.num_tiles : 1));
+  if ((al & 15) == 0)
+    hipLaunchKernelGGL(up::up_compact_kernel<16>, grid, dim3(up::kCompactThreads), 0, stream, a);
+  else if ((al & 7) == 0)
+    hipLaunchKernelGGL(up::up_compact_kernel<8>, grid, dim3(up::kCompactThreads), 0, stream, a);
+  else if ((al & 3) == 0)
+    hipLaunchKernelGGL(up::up_compact_kernel<4>, grid, dim3(up::kCompactThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(up::up_compact_kernel<1>, grid, dim3(up::kCompactThreads), 0, stream, a);
+  return up::check_launch("up_compact_kernel");
+}
+
+size_t up_history_bytes(int num_seqs, int capacity) {
+  if (num_seqs < 0 || capacity < 0) return 0;
+  return sizeof(int32_t) * (up::kLedgerHeader + (size_t)num_seqs + 2 * (size_t)num_seqs * capacity);
+}
+
+up_status up_history_init(void* ledger, int num_seqs, int capacity, hipStream_t stream) {
+  up::clear_error();
+  if (!ledger) return up::set_error(UP_ERR_INVALID, "ledger is NULL");
+  if (num_seqs < 0 || capacity < 1) return up::set_error(UP_ERR_INVALID, "need num_seqs >= 0, capacity >= 1");
+  up_status st = up::check_device();
+  if (st != UP_OK) return st;
+  hipLaunchKernelGGL(up::up_history_init_kernel, dim3((unsigned)up::ceil_div(num_seqs + 1, 256)),
+                     dim3(256), 0, stream, static_cast<int32_t*>(ledger), num_seqs, capacity);
+  return up::check_launch("up_history_init_kernel");
+}
+
+up_status up_drop_history(void* ledger, int num_seqs, int capacity, int layer_id,
+                          const int32_t* cu_seqlens_out, hipStream_t stream) {
+  up::clear_error();
+  if (!ledger || !cu_seqlens_out) return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if (num_seqs < 0 || capacity < 1) return up::set_error(UP_ERR_INVALID, "need num_seqs >= 0, capacity >= 1");
+  if (num_seqs == 0) return UP_OK;
+  up_status st = up::check_device();
+  if (st != UP_OK) return st;
+  hipLaunchKernelGGL(up::up_history_append_kernel, dim3((unsigned)up::ceil_div(num_seqs, 256)),
+                     dim3(256), 0, stream, static_cast<int32_t*>(ledger), num_seqs, capacity,
+                     layer_id, cu_seqlens_out);
+  return up::check_launch("up_history_append_kernel");
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <string>
+
+#include "uniprefill.h"
+
+namespace up {
+
+// Thread-local error message; set_error returns the status for chaining.
+up_status set_error(up_status st, const char* fmt, ...);
+void clear_error();
+
+// Checks (once per device) that the current device is gfx950.
+up_status check_device();
+
+// Host-side validation of a packed batch; fills T and max length.
+up_status check_cu_seqlens(int num_seqs, const int32_t* cu_h, int64_t* T, int* max_len);
+
+// Turns the last HIP launch error into UP_ERR_HIP.
+up_status check_launch(const char* what);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Geometry of the scoring kernels for one call (computed on the host).
+struct ScoreGeometry {
+  int rows_per_wg;   // query rows one workgroup holds in registers
+  int waves;         // waves per workgroup
+  int rg;            // row groups per KV head
+  int ck;            // keys per workgroup chunk
+  int max_chunks;    // chunks of the longest request
+  size_t off_partial, off_bias, off_colpart, bytes;
+};
+
+ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv,
+                             int head_dim, int n_query);
+
+// Number of blocks a compaction tile spans for block size G.
+int compact_tile_blocks(int block);
+
+}  // namespace up

@@ -1,0 +1,608 @@
+// Steps 1-3 of the pruning path: tail-query importance scores and block means.
+//
+// Method (UniPrefill page "中国科学院与腾讯微信合作解决AI排队等待问题", §二 steps 1-2
+// and §三): the last n tokens of a request query every key with a softmax
+// normalised per query row; the probabilities summed over query rows and
+// heads give each token's score, averaged over G-token blocks.
+//
+// Exact column sums need each row's final softmax statistics, which exist
+// only after the whole key sweep, so S = Q_tail K^T is computed twice
+// (recomputing is far cheaper than writing S to HBM):
+//   pass A  up_rowstats_kernel   per (request, KV head, key chunk): bf16
+//           MFMA S tiles with keys on the MFMA M axis, so each lane owns one
+//           query row and reduces a running (max, sum) in registers.
+//   combine up_rowstats_combine_kernel  merges the chunk partials into one
+//           log2-domain bias per row: m * c + log2(l), c = scale * log2(e).
+//   pass B  up_colsum_kernel    same tiles with queries on the M axis, so each
+//           lane owns one key and sums exp2(s * c - bias) over its rows in
+//           registers; waves meet in LDS, one partial per (KV head, row group)
+//           is written per key.
+//   epilogue up_blockmean_kernel sums the partials over KV heads in a fixed
+//           order (token score) and averages each block (block score).
+// No floating-point atomics anywhere: results are bitwise reproducible.
+#include <math.h>
+
+#include "up_internal.h"
+
+namespace up {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int KT = 64;  // keys per LDS tile (two 32-wide MFMA tiles)
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_inff();
+
+struct ScoreArgs {
+  const int32_t* cu_seqlens;
+  const int32_t* cu_blocks;
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t q_tok, q_head, k_tok, k_head;
+  int num_seqs, hq, hkv, rgqa, n_query, block;
+  int ck, max_chunks, rg, rows_per_wg;
+  int64_t num_groups;  // B * hkv * max_chunks (request, KV head, key chunk) groups
+  float c;  // scale * log2(e)
+  float2* partial;  // [B][hq][n_query][max_chunks] (raw max, sum of exp2)
+  float* bias;      // [B][hq][n_query]
+  float* colpart;   // [hkv * rg][T]
+  int64_t T;
+  float* token_scores;
+  float* block_scores;
+  int64_t num_blocks;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Work decode shared by both passes.  Workgroups that read the same K chunk
+// (the rg row groups of one (request, KV head, chunk) group) get ids that are
+// equal mod 8, so they run on the same XCD (ids are dealt round-robin over the
+// 8 XCDs) and are dispatched close together: their K re-reads hit that XCD's
+// L2.  Consecutive groups on one XCD are consecutive chunks of the same head,
+// which share the query rows.
+struct Work {
+  int req, g, chunk, rgi;
+  bool valid;
+};
+
+__device__ __forceinline__ Work decode_work(const ScoreArgs& a) {
+  const int64_t w = blockIdx.x;
+  const int64_t span = 8 * (int64_t)a.rg;
+  const int64_t blk = w / span, rem = w - blk * span;
+  Work wk;
+  wk.rgi = (int)(rem >> 3);
+  const int64_t q = blk * 8 + (rem & 7);
+  wk.valid = q < a.num_groups;
+  const int64_t per_req = (int64_t)a.hkv * a.max_chunks;
+  wk.req = (int)(q / per_req);
+  const int64_t r2 = q - (int64_t)wk.req * per_req;
+  wk.g = (int)(r2 / a.max_chunks);
+  wk.chunk = (int)(r2 - (int64_t)wk.g * a.max_chunks);
+  return wk;
+}
+
+// Key rows of one tile: global -> registers -> LDS (double-buffered by caller).
+template <int D, int W>
+struct KTile {
+  static constexpr int VPR = D / 8;                  // 16-byte vectors per key row
+  static constexpr int VPT = KT * VPR / (64 * W);    // vectors per thread
+  static constexpr int STRIDE = D + 8;               // LDS row stride, elements
+  static_assert(KT * VPR % (64 * W) == 0, "tile not divisible among threads");
+  u32x4_t r[VPT];
+
+  __device__ __forceinline__ void load(const uint16_t* kbase, int64_t k_tok, int tkey0,
+                                       int key_end, int tid) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = i * 64 * W + tid;
+      const int row = e / VPR, col = e % VPR;
+      const int key = tkey0 + row;
+      if (key < key_end)
+        r[i] = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)key * k_tok + col * 8);
+      else
+        r[i] = (u32x4_t){0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = i * 64 * W + tid;
+      const int row = e / VPR, col = e % VPR;
+      *reinterpret_cast<u32x4_t*>(lds + row * STRIDE + col * 8) = r[i];
+    }
+  }
+};
+
+// Query fragments of the lane's rows.  Row rho of KV group g is query head
+// g*rgqa + rho/n_eff at tail position rho%n_eff.  The same registers serve as
+// the MFMA B operand in pass A and the A operand in pass B: lane l holds row
+// (l % 32) of each 32-row tile and dims [16s + 8(l/32), +8) of k-step s.
+template <int D, int NT>
+__device__ __forceinline__ void load_q(const ScoreArgs& a, int s0, int qpos0, int n_eff, int R,
+                                       int g, int row0, int lane, bf16x8_t (&qf)[NT][D / 16],
+                                       int (&ipos)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int rho = row0 + t * 32 + (lane & 31);
+    if (rho < R) {
+      const int hl = rho / n_eff, ti = rho - hl * n_eff;
+      const int h = g * a.rgqa + hl;
+      const uint16_t* p = a.q + (int64_t)(s0 + qpos0 + ti) * a.q_tok + (int64_t)h * a.q_head +
+                          (lane >> 5) * 8;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[t][s] = load_bf16x8(p + s * 16);
+      ipos[t] = qpos0 + ti;
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[t][s] = (bf16x8_t){};
+      ipos[t] = 0x7fffffff;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass A: per-row running max and sum of exp2 over one key chunk.
+// ---------------------------------------------------------------------------
+template <int D, int NT, int W>
+__global__ void __launch_bounds__(64 * W) up_rowstats_kernel(ScoreArgs a) {
+  using Tile = KTile<D, W>;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[2][KT * Tile::STRIDE];
+
+  const Work wk = decode_work(a);
+  if (!wk.valid) return;
+  const int chunk = wk.chunk, g = wk.g, rgi = wk.rgi, req = wk.req;
+  const int s0 = a.cu_seqlens[req];
+  const int L = a.cu_seqlens[req + 1] - s0;
+  const int key0 = chunk * a.ck;
+  const int n_eff = min(a.n_query, L);
+  const int R = a.rgqa * n_eff;
+  const int wg_row0 = rgi * (NT * 32 * W);
+  if (key0 >= L || wg_row0 >= R) return;  // uniform over the workgroup
+  const int key1 = min(L, key0 + a.ck);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row0 = wg_row0 + wave * NT * 32;
+  const int qpos0 = L - n_eff;
+  const float C = a.c;
+
+  bf16x8_t qf[NT][D / 16];
+  int ipos[NT];
+  load_q<D, NT>(a, s0, qpos0, n_eff, R, g, row0, lane, qf, ipos);
+
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m_run[t] = kNegInf;
+    l_run[t] = 0.f;
+  }
+
+  const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
+  const int ntiles = (key1 - key0 + KT - 1) / KT;
+  Tile tile;
+  tile.load(kbase, a.k_tok, key0, key1, tid);
+  tile.store(kl[0], tid);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int tkey0 = key0 + it * KT;
+    if (it + 1 < ntiles) tile.load(kbase, a.k_tok, tkey0 + KT, key1, tid);
+
+#pragma unroll
+    for (int mt = 0; mt < KT / 32; ++mt) {
+      bf16x8_t af[D / 16];
+      const uint16_t* lrow = kl[buf] + (mt * 32 + (lane & 31)) * Tile::STRIDE + (lane >> 5) * 8;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) af[s] = load_bf16x8(lrow + s * 16);
+      const int mkey0 = tkey0 + mt * 32;
+      const bool need_mask = (mkey0 + 31 > qpos0) || (mkey0 + 31 >= key1);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) acc = mfma32(af[s], qf[t][s], acc);
+        if (need_mask) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int j = mkey0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (j >= key1 || j > ipos[t]) acc[v] = kNegInf;
+          }
+        }
+        float mx = acc[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
+        const float mnew = fmaxf(m_run[t], mx);
+        const float mc = (mnew == kNegInf) ? 0.f : mnew * C;
+        float sum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum += fast_exp2(fmaf(acc[v], C, -mc));
+        l_run[t] = fmaf(l_run[t], fast_exp2(fmaf(m_run[t], C, -mc)), sum);
+        m_run[t] = mnew;
+      }
+    }
+    if (it + 1 < ntiles) tile.store(kl[buf ^ 1], tid);
+    __syncthreads();
+  }
+
+  // Merge the two half-waves (same row, disjoint keys) and write the partial.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float mo = __shfl_xor(m_run[t], 32);
+    const float lo = __shfl_xor(l_run[t], 32);
+    const float M = fmaxf(m_run[t], mo);
+    const float mc = (M == kNegInf) ? 0.f : M * C;
+    const float l = l_run[t] * fast_exp2(fmaf(m_run[t], C, -mc)) + lo * fast_exp2(fmaf(mo, C, -mc));
+    const int rho = row0 + t * 32 + lane;
+    if (lane < 32 && rho < R) {
+      const int hl = rho / n_eff, ti = rho - hl * n_eff;
+      const int h = g * a.rgqa + hl;
+      a.partial[(((int64_t)req * a.hq + h) * a.n_query + ti) * a.max_chunks + chunk] =
+          make_float2(M, l);
+    }
+  }
+}
+
+// Combine the chunk partials of each row: bias = m * c + log2(l).
+__global__ void up_rowstats_combine_kernel(ScoreArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.num_seqs * a.hq * a.n_query;
+  if (idx >= total) return;
+  const int ti = (int)(idx % a.n_query);
+  const int req = (int)(idx / ((int64_t)a.n_query * a.hq));
+  const int L = a.cu_seqlens[req + 1] - a.cu_seqlens[req];
+  const int n_eff = min(a.n_query, L);
+  if (ti >= n_eff) return;
+  const int nch = (L + a.ck - 1) / a.ck;
+  const float2* pp = a.partial + idx * a.max_chunks;
+  float M = kNegInf;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, pp[c].x);
+  const float mc = M * a.c;
+  float l = 0.f;
+  for (int c = 0; c < nch; ++c) l += pp[c].y * fast_exp2(fmaf(pp[c].x, a.c, -mc));
+  a.bias[idx] = mc + log2f(l);
+}
+
+// ---------------------------------------------------------------------------
+// Pass B: column sums of the normalised probabilities over the chunk's keys.
+// ---------------------------------------------------------------------------
+template <int D, int NT, int W>
+__global__ void __launch_bounds__(64 * W) up_colsum_kernel(ScoreArgs a) {
+  using Tile = KTile<D, W>;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[2][KT * Tile::STRIDE];
+  __shared__ float colbuf[2][W][KT];
+
+  const Work wk = decode_work(a);
+  if (!wk.valid) return;
+  const int chunk = wk.chunk, g = wk.g, rgi = wk.rgi, req = wk.req;
+  const int s0 = a.cu_seqlens[req];
+  const int L = a.cu_seqlens[req + 1] - s0;
+  const int key0 = chunk * a.ck;
+  const int n_eff = min(a.n_query, L);
+  const int R = a.rgqa * n_eff;
+  const int wg_row0 = rgi * (NT * 32 * W);
+  if (key0 >= L || wg_row0 >= R) return;
+  const int key1 = min(L, key0 + a.ck);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row0 = wg_row0 + wave * NT * 32;
+  const int qpos0 = L - n_eff;
+  const float C = a.c;
+
+  bf16x8_t qf[NT][D / 16];
+  int ipos_unused[NT];
+  load_q<D, NT>(a, s0, qpos0, n_eff, R, g, row0, lane, qf, ipos_unused);
+
+  // Output element v of a 32x32 tile in lane l sits at row 8(v/4) + 4(l/32) + v%4.
+  float bv[NT][16];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rho = row0 + t * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (rho < R) {
+        const int hl = rho / n_eff, ti = rho - hl * n_eff;
+        bv[t][v] = a.bias[((int64_t)req * a.hq + g * a.rgqa + hl) * a.n_query + ti];
+      } else {
+        bv[t][v] = kPosInf;
+      }
+    }
+  }
+
+  const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
+  float* colout = a.colpart + ((int64_t)g * a.rg + rgi) * a.T + s0;
+  const int ntiles = (key1 - key0 + KT - 1) / KT;
+  Tile tile;
+  tile.load(kbase, a.k_tok, key0, key1, tid);
+  tile.store(kl[0], tid);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int tkey0 = key0 + it * KT;
+    if (it + 1 < ntiles) tile.load(kbase, a.k_tok, tkey0 + KT, key1, tid);
+
+#pragma unroll
+    for (int nt = 0; nt < KT / 32; ++nt) {
+      bf16x8_t kf[D / 16];
+      const uint16_t* lrow = kl[buf] + (nt * 32 + (lane & 31)) * Tile::STRIDE + (lane >> 5) * 8;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) kf[s] = load_bf16x8(lrow + s * 16);
+      const int key = tkey0 + nt * 32 + (lane & 31);
+      const bool need_mask = (tkey0 + nt * 32 + 31 > qpos0) || (tkey0 + nt * 32 + 31 >= key1);
+      float col = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) acc = mfma32(qf[t][s], kf[s], acc);
+        if (!need_mask) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) col += fast_exp2(fmaf(acc[v], C, -bv[t][v]));
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rho = row0 + t * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int ti = rho < R ? rho % n_eff : 0;
+            const bool ok = (key < key1) && (key <= qpos0 + ti);
+            col += ok ? fast_exp2(fmaf(acc[v], C, -bv[t][v])) : 0.f;
+          }
+        }
+      }
+      col += __shfl_xor(col, 32);
+      if (lane < 32) colbuf[buf][wave][nt * 32 + lane] = col;
+    }
+    if (it + 1 < ntiles) tile.store(kl[buf ^ 1], tid);
+    __syncthreads();
+    if (tid < KT) {
+      const int key = tkey0 + tid;
+      if (key < key1) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) s += colbuf[buf][w][tid];
+        colout[key] = s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue: token score = fixed-order sum of the per-(KV head, row group)
+// partials; block score = mean over the block's tokens.  One wave per block.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 4 + wave;
+  if (b >= a.num_blocks) return;
+  // request owning block b: last r with cu_blocks[r] <= b
+  int lo = 0, hi = a.num_seqs;  // invariant: cu_blocks[lo] <= b < cu_blocks[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
+  }
+  const int r = lo;
+  const int s0 = a.cu_seqlens[r];
+  const int L = a.cu_seqlens[r + 1] - s0;
+  const int lb = (int)(b - a.cu_blocks[r]);
+  const int j0 = lb * a.block, j1 = min(j0 + a.block, L);
+  // only the row groups that hold rows of this request wrote partials
+  const int n_eff = min(a.n_query, L);
+  const int rg_used = (a.rgqa * n_eff + a.rows_per_wg - 1) / a.rows_per_wg;
+  float sum = 0.f;
+  for (int j = j0 + lane; j < j1; j += 64) {
+    float c = 0.f;
+    for (int g = 0; g < a.hkv; ++g)
+      for (int rgi = 0; rgi < rg_used; ++rgi)
+        c += a.colpart[((int64_t)g * a.rg + rgi) * a.T + s0 + j];
+    if (a.token_scores) a.token_scores[s0 + j] = c;
+    sum += c;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane == 0) a.block_scores[b] = sum / (float)(j1 - j0);
+}
+
+// Compile-time tiling per head_dim: NT 32-row tiles per wave, W waves.
+template <int D> struct Tiling;
+template <> struct Tiling<64> { static constexpr int NT = 2, W = 8; };
+template <> struct Tiling<128> { static constexpr int NT = 2, W = 8; };
+template <> struct Tiling<256> { static constexpr int NT = 1, W = 8; };
+
+int rows_per_wg_for(int d) {
+  switch (d) {
+    case 64: return Tiling<64>::NT * 32 * Tiling<64>::W;
+    case 128: return Tiling<128>::NT * 32 * Tiling<128>::W;
+    default: return Tiling<256>::NT * 32 * Tiling<256>::W;
+  }
+}
+
+template <int D>
+up_status launch_passes(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int NT = Tiling<D>::NT, W = Tiling<D>::W;
+  hipLaunchKernelGGL((up_rowstats_kernel<D, NT, W>), grid, dim3(64 * W), 0, st, a);
+  up_status s = check_launch("up_rowstats_kernel");
+  if (s != UP_OK) return s;
+  const int64_t rows = (int64_t)a.num_seqs * a.hq * a.n_query;
+  hipLaunchKernelGGL(up_rowstats_combine_kernel, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0,
+                     st, a);
+  s = check_launch("up_rowstats_combine_kernel");
+  if (s != UP_OK) return s;
+  hipLaunchKernelGGL((up_colsum_kernel<D, NT, W>), grid, dim3(64 * W), 0, st, a);
+  return check_launch("up_colsum_kernel");
+}
+
+}  // namespace
+
+ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv, int head_dim,
+                             int n_query) {
+  ScoreGeometry g{};
+  g.rows_per_wg = rows_per_wg_for(head_dim);
+  const int rgqa = hkv > 0 ? hq / hkv : 1;
+  const int64_t rmax = (int64_t)rgqa * (n_query < max_len ? n_query : max_len);
+  g.rg = (int)(rmax > 0 ? ceil_div(rmax, g.rows_per_wg) : 1);
+  g.ck = 0;  // chosen by the caller once lengths are known
+  g.max_chunks = 0;
+  (void)num_seqs;
+  (void)T;
+  return g;
+}
+
+}  // namespace up
+
+extern "C" up_status up_score_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int hq,
+                                             int hkv, int head_dim, int n_query, size_t* bytes);
+
+namespace {
+
+// Key chunk per workgroup: the largest power of two in [256, 4096] that
+// still gives >= 1024 workgroups (four per CU) for this batch.
+int choose_ck(int num_seqs, const int32_t* cu_h, int hkv, int rg) {
+  int ck = 4096;
+  while (ck > 256) {
+    int64_t wgs = 0;
+    for (int r = 0; r < num_seqs; ++r)
+      wgs += up::ceil_div(cu_h[r + 1] - cu_h[r], ck) * (int64_t)hkv * rg;
+    if (wgs >= 1024) break;
+    ck >>= 1;
+  }
+  return ck;
+}
+
+struct Layout {
+  up::ScoreGeometry g;
+  size_t bytes;
+};
+
+up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int head_dim,
+                       int n_query, Layout* out) {
+  int64_t T;
+  int max_len;
+  up_status st = up::check_cu_seqlens(num_seqs, cu_h, &T, &max_len);
+  if (st != UP_OK) return st;
+  if (hq < 1 || hkv < 1 || hq > 1024 || hq % hkv != 0)
+    return up::set_error(UP_ERR_INVALID, "need 1 <= hq <= 1024, hkv >= 1, hq %% hkv == 0 (hq=%d hkv=%d)",
+                         hq, hkv);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return up::set_error(UP_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", head_dim);
+  if (n_query < 1 || n_query > 4096)
+    return up::set_error(UP_ERR_UNSUPPORTED, "n_query %d not in [1, 4096]", n_query);
+  up::ScoreGeometry g = up::score_geometry(num_seqs, T, max_len, hq, hkv, head_dim, n_query);
+  g.ck = choose_ck(num_seqs, cu_h, hkv, g.rg);
+  g.max_chunks = (int)(max_len > 0 ? up::ceil_div(max_len, g.ck) : 1);
+  size_t off = 0;
+  g.off_partial = off;
+  off = up::align_up(off + (size_t)num_seqs * hq * n_query * g.max_chunks * sizeof(float2), 256);
+  g.off_bias = off;
+  off = up::align_up(off + (size_t)num_seqs * hq * n_query * sizeof(float), 256);
+  g.off_colpart = off;
+  off = up::align_up(off + (size_t)hkv * g.rg * (size_t)T * sizeof(float), 256);
+  g.bytes = off > 0 ? off : 256;
+  out->g = g;
+  out->bytes = g.bytes;
+  return UP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+up_status up_score_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int hq, int hkv,
+                                  int head_dim, int n_query, size_t* bytes) {
+  up::clear_error();
+  if (bytes == nullptr) return up::set_error(UP_ERR_INVALID, "bytes is NULL");
+  Layout lay;
+  up_status st = score_layout(num_seqs, cu_seqlens_h, hq, hkv, head_dim, n_query, &lay);
+  if (st != UP_OK) return st;
+  *bytes = lay.bytes;
+  return UP_OK;
+}
+
+up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                   const int32_t* cu_blocks_d, const void* q, int64_t q_tok_stride,
+                   int64_t q_head_stride, int hq, const void* k, int64_t k_tok_stride,
+                   int64_t k_head_stride, int hkv, int head_dim, int n_query, int block, float scale,
+                   float* token_scores, float* block_scores, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  up::clear_error();
+  Layout lay;
+  up_status st = score_layout(num_seqs, cu_seqlens_h, hq, hkv, head_dim, n_query, &lay);
+  if (st != UP_OK) return st;
+  if (block < 16 || block > 256 || (block & (block - 1)) != 0)
+    return up::set_error(UP_ERR_UNSUPPORTED, "block %d is not a power of two in [16, 256]", block);
+  if (!(scale >= 0.f) || !isfinite(scale))
+    return up::set_error(UP_ERR_INVALID, "scale must be finite and >= 0 (0 = 1/sqrt(head_dim))");
+  const int64_t T = cu_seqlens_h[num_seqs];
+  int64_t N = 0;
+  for (int r = 0; r < num_seqs; ++r) N += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], block);
+  if (num_seqs == 0 || T == 0) return UP_OK;  // nothing to score
+  if (!cu_seqlens_d || !cu_blocks_d || !q || !k || !block_scores || !workspace)
+    return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if (((uintptr_t)q & 15) || ((uintptr_t)k & 15) || (q_tok_stride & 7) || (q_head_stride & 7) ||
+      (k_tok_stride & 7) || (k_head_stride & 7))
+    return up::set_error(UP_ERR_UNSUPPORTED,
+                         "q/k must be 16-byte aligned with strides that are multiples of 8 elements");
+  if (q_tok_stride < 0 || q_head_stride < 0 || k_tok_stride < 0 || k_head_stride < 0)
+    return up::set_error(UP_ERR_INVALID, "negative stride");
+  if ((uintptr_t)workspace & 255) return up::set_error(UP_ERR_INVALID, "workspace not 256-byte aligned");
+  if (workspace_bytes < lay.bytes)
+    return up::set_error(UP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes,
+                         lay.bytes);
+  st = up::check_device();
+  if (st != UP_OK) return st;
+
+  up::ScoreArgs a{};
+  char* ws = static_cast<char*>(workspace);
+  a.cu_seqlens = cu_seqlens_d;
+  a.cu_blocks = cu_blocks_d;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.q_tok = q_tok_stride;
+  a.q_head = q_head_stride;
+  a.k_tok = k_tok_stride;
+  a.k_head = k_head_stride;
+  a.num_seqs = num_seqs;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.rgqa = hq / hkv;
+  a.n_query = n_query;
+  a.block = block;
+  a.ck = lay.g.ck;
+  a.max_chunks = lay.g.max_chunks;
+  a.rg = lay.g.rg;
+  a.rows_per_wg = lay.g.rows_per_wg;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
+  a.c = sc * 1.4426950408889634f;
+  a.partial = reinterpret_cast<float2*>(ws + lay.g.off_partial);
+  a.bias = reinterpret_cast<float*>(ws + lay.g.off_bias);
+  a.colpart = reinterpret_cast<float*>(ws + lay.g.off_colpart);
+  a.T = T;
+  a.token_scores = token_scores;
+  a.block_scores = block_scores;
+  a.num_blocks = N;
+
+  a.num_groups = (int64_t)num_seqs * hkv * a.max_chunks;
+  const int64_t nwg = up::ceil_div(a.num_groups, 8) * 8 * a.rg;
+  if (nwg > 0x7fffffff) return up::set_error(UP_ERR_UNSUPPORTED, "grid too large");
+  dim3 grid((unsigned)nwg);
+  switch (head_dim) {
+    case 64: st = up::launch_passes<64>(a, grid, stream); break;
+    case 128: st = up::launch_passes<128>(a, grid, stream); break;
+    default: st = up::launch_passes<256>(a, grid, stream); break;
+  }
+  if (st != UP_OK) return st;
+  if (N > 0) {
+    hipLaunchKernelGGL(up::up_blockmean_kernel, dim3((unsigned)up::ceil_div(N, 4)), dim3(256), 0,
+                       stream, a);
+    st = up::check_launch("up_blockmean_kernel");
+  }
+  return st;
+}
+
+}  // extern "C"
