@@ -145,8 +145,11 @@ up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_
  * block_scores  fp32 [N], finite and >= 0.
  * block_mask    uint8 [N] (written: 1 keep, 0 drop).
  * kept_tokens   int32 [B] (written: tokens in kept blocks).
- * top_p in (0, 1]; sink, tail >= 0; at most 16384 blocks per request.
- * Sums run in fp64 in a fixed order (deterministic).
+ * top_p in (0, 1]; sink, tail >= 0; at most 2^24 blocks per request.
+ * Masses are summed exactly as 63-bit fixed point relative to the request's
+ * largest score (deterministic in any order); a decision can differ from
+ * exact real arithmetic only when the cumulative mass lies within
+ * N * 2^-(62 - ceil(log2(N+1))) of the largest score from p * total.
  */
 up_status up_select_topp(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                          const int32_t* cu_blocks_d, const float* block_scores, int block,

@@ -103,7 +103,7 @@ def test_select_rejects_bad_arguments():
                                (0.9, -1, 128, "sink")]:
         st = lib.up_select_topp(1, cu.data_ptr(), 16, 16, 16, 64, p, sink, tail, 16, 16, None)
         assert st == 1 and msg in U.up_last_error()
-    big = torch.tensor([0, 64 * 16385], dtype=torch.int32)
+    big = torch.tensor([0, 64 * ((1 << 24) + 1)], dtype=torch.int32)
     st = lib.up_select_topp(1, big.data_ptr(), 16, 16, 16, 64, 0.99, 128, 128, 16, 16, None)
     assert st == 2 and "blocks" in U.up_last_error()
 

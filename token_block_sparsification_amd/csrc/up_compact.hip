@@ -14,6 +14,10 @@
 // the inclusive count, and copies its kept blocks.  Because the mask is per
 // block, a kept block is a run of G consecutive rows, copied as one flat
 // byte range with wide vector loads and stores; dropped rows are never read.
+// Every status word carries its state and its count in one 64-bit atomic and
+// no tile reads data another tile wrote, so relaxed device-scope atomics are
+// enough: release/acquire at device scope would write back / invalidate the
+// XCD's L2 on every publish and poll, which stalls the copy.
 // The last workgroup to finish (a done counter) clears the tile status words
 // and both counters, so the next call starts from a clean workspace without
 // a separate clearing launch; up_compact_workspace_init prepares a new one.
@@ -148,37 +152,41 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_kernel(CompactArgs
       const int64_t agg = __shfl(incl, 63);
       if (lane < nblk) s_dst[lane] = incl - ksize;
 
+      // Publish this tile's count, then look back a window of 64
+      // predecessors per round trip: lane i reads tile (hi - i); the nearest
+      // tile that already has an inclusive prefix ends the walk.
+      if (lane == 0)
+        __hip_atomic_store(&a.flags[t], (t == 0 ? kFlagIncl : kFlagAgg) | (uint64_t)agg,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       int64_t excl = 0;
-      if (lane == 0) {
-        if (t == 0) {
-          __hip_atomic_store(&a.flags[0], kFlagIncl | (uint64_t)agg, __ATOMIC_RELEASE,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          __hip_atomic_store(&a.flags[t], kFlagAgg | (uint64_t)agg, __ATOMIC_RELEASE,
-                             __HIP_MEMORY_SCOPE_AGENT);
-          int64_t p = t - 1;
-          while (p >= 0) {
-            uint64_t f = 0;
+      if (t > 0) {
+        int64_t hi = t - 1;
+        for (;;) {
+          const int64_t p = hi - lane;
+          uint64_t f = kFlagIncl;  // before tile 0: an inclusive prefix of 0
+          if (p >= 0) {
             int spins = 0;
             for (;;) {
-              f = __hip_atomic_load(&a.flags[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+              f = __hip_atomic_load(&a.flags[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               if ((f >> 62) != 0 || ++spins >= kSpinLimit) break;
               __builtin_amdgcn_s_sleep(1);
             }
-            if ((f >> 62) == 0) {  // predecessor never published: give up, flag it
-              atomicOr(&a.ctl[2], 1u);
-              break;
-            }
-            excl += (int64_t)(f & kValueMask);
-            if ((f >> 62) == 2) break;
-            --p;
           }
-          __hip_atomic_store(&a.flags[t], kFlagIncl | (uint64_t)(excl + agg), __ATOMIC_RELEASE,
-                             __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t incl_lanes = __ballot((f >> 62) == 2);
+          const int stop = incl_lanes ? __ffsll((unsigned long long)incl_lanes) - 1 : 63;
+          if (lane <= stop && (f >> 62) == 0) atomicOr(&a.ctl[2], 1u);  // predecessor never published
+          int64_t v = (lane <= stop) ? (int64_t)(f & kValueMask) : 0;
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+          excl += v;
+          if (incl_lanes) break;
+          hi -= 64;
         }
-        s_excl = excl;
+        if (lane == 0)
+          __hip_atomic_store(&a.flags[t], kFlagIncl | (uint64_t)(excl + agg), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
-      excl = __shfl(excl, 0);
+      if (lane == 0) s_excl = excl;
 
       // Requests whose last block is in this tile (and empty requests right
       // after them) end at this block's inclusive count.
@@ -219,7 +227,7 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_kernel(CompactArgs
   // look-back before it counted itself done).
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.ctl[1], 1u, __ATOMIC_ACQ_REL,
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ctl[1], 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == gridDim.x - 1) ? 1 : 0;
   }

@@ -251,9 +251,11 @@ __global__ void __launch_bounds__(64 * W) up_rowstats_kernel(ScoreArgs a) {
   }
 }
 
-// Combine the chunk partials of each row: bias = m * c + log2(l).
-__global__ void up_rowstats_combine_kernel(ScoreArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Combine the chunk partials of each row: bias = m * c + log2(l).  One wave
+// per row, lanes over chunks, fixed-order butterfly reductions.
+__global__ void __launch_bounds__(256) up_rowstats_combine_kernel(ScoreArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
   const int64_t total = (int64_t)a.num_seqs * a.hq * a.n_query;
   if (idx >= total) return;
   const int ti = (int)(idx % a.n_query);
@@ -264,11 +266,15 @@ __global__ void up_rowstats_combine_kernel(ScoreArgs a) {
   const int nch = (L + a.ck - 1) / a.ck;
   const float2* pp = a.partial + idx * a.max_chunks;
   float M = kNegInf;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, pp[c].x);
+  for (int c = lane; c < nch; c += 64) M = fmaxf(M, pp[c].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   const float mc = M * a.c;
   float l = 0.f;
-  for (int c = 0; c < nch; ++c) l += pp[c].y * fast_exp2(fmaf(pp[c].x, a.c, -mc));
-  a.bias[idx] = mc + log2f(l);
+  for (int c = lane; c < nch; c += 64) l += pp[c].y * fast_exp2(fmaf(pp[c].x, a.c, -mc));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+  if (lane == 0) a.bias[idx] = mc + log2f(l);
 }
 
 // ---------------------------------------------------------------------------
@@ -430,7 +436,7 @@ up_status launch_passes(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   up_status s = check_launch("up_rowstats_kernel");
   if (s != UP_OK) return s;
   const int64_t rows = (int64_t)a.num_seqs * a.hq * a.n_query;
-  hipLaunchKernelGGL(up_rowstats_combine_kernel, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0,
+  hipLaunchKernelGGL(up_rowstats_combine_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0,
                      st, a);
   s = check_launch("up_rowstats_combine_kernel");
   if (s != UP_OK) return s;

@@ -5,21 +5,36 @@
 // set holding p of the total importance is kept, and the blocks covering the
 // first and the last 128 tokens are exempt from pruning.
 //
-// One workgroup per request.  Each block becomes a 64-bit key
-//   (forced ? 0xFFFFFFFF : order-preserving bits of its score) << 32 | ~index
-// so a descending sort puts the forced blocks first and the rest in
-// (score desc, index asc) order.  The keys are sorted in LDS with a bitonic
-// network; an fp64 exclusive scan over the sorted scores (fixed order, no
-// atomics) then keeps position k iff it is forced or its exclusive prefix is
-// still below p * total.
+// Rule: forced blocks count toward the mass; optional blocks are taken in
+// (score desc, index asc) order while the kept mass is below p * total.  The
+// kept optional blocks are therefore exactly those ranked before a cutoff
+// block, so no full sort is needed, only the cutoff:
+//
+//   1. One workgroup per request.  Each block's score becomes an integer mass
+//      m = floor(score / max_score * 2^S) (S chosen so the sum fits 63 bits),
+//      so every sum below is exact and independent of summation order: the
+//      result is bitwise deterministic.
+//   2. R = ceil(p * total) - forced mass is the optional mass still needed.
+//   3. Radix select, most significant 8-bit digit first, over the 32-bit
+//      order-preserving key of each optional block's score: an LDS histogram
+//      of (count, mass) per digit, then one wave scans the 256 buckets from
+//      the top and finds the bucket where the mass from above reaches R.
+//      Four passes give the exact cutoff score v* and the mass above it.
+//   4. Blocks with score v* are tied; the lowest-index ones are kept until the
+//      mass reaches R (a block-wide prefix count over index order).
+// Fixed point differs from exact fp64 sums by < N * 2^-S of the top score, so
+// a decision can differ from an fp64 evaluation only when the cumulative
+// mass is within that distance of p * total.
+#include <math.h>
+
 #include "up_internal.h"
 
 namespace up {
 namespace {
 
-constexpr int kSelectThreads = 1024;
+constexpr int kSelectThreads = 256;
 constexpr int kSelectWaves = kSelectThreads / 64;
-constexpr int kMaxBlocksPerRequest = 16384;
+constexpr int64_t kMaxBlocksPerRequest = 1 << 24;
 
 struct SelectArgs {
   const int32_t* cu_seqlens;
@@ -42,39 +57,105 @@ __device__ __forceinline__ bool is_forced(int i, int L, int G, int sink, int tai
   return j0 < sink || j1 > L - tail;
 }
 
-// Block-wide exclusive scan of one double per thread (fixed order).
-__device__ double block_exclusive_scan(double x, double* wave_tot, double* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double incl = x;
+__device__ __forceinline__ uint64_t mass_of(float s, double scale) {
+  const double m = (double)s * scale;
+  return m > 0.0 ? (uint64_t)m : 0ull;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+struct SelectShared {
+  uint32_t cnt[256];
+  uint64_t mass[256];
+  uint64_t red[kSelectWaves];
+  float redf[kSelectWaves];
+  int redi[kSelectWaves];
+  // decision state (written by wave 0, read by all after a barrier)
+  uint32_t prefix;       // known high digits of the cutoff key
+  uint64_t above;        // optional mass with key above the current bucket range
+  int64_t need;          // R: optional mass still needed (<= 0: none)
+  int all_optional;      // the optional mass never reaches R: keep every block
+  uint64_t tie_mass;     // mass of one block at the cutoff key
+  uint64_t tie_keep;     // how many tied blocks (lowest index first) are kept
+};
+
+// Block-wide reductions (fixed order: wave butterfly, then waves in order).
+__device__ uint64_t block_sum_u64(uint64_t v, SelectShared& sh) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t s = 0;
+  for (int w = 0; w < kSelectWaves; ++w) s += sh.red[w];
+  return s;
+}
+
+__device__ float block_max(float v, SelectShared& sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.redf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = sh.redf[0];
+  for (int w = 1; w < kSelectWaves; ++w) m = fmaxf(m, sh.redf[w]);
+  return m;
+}
+
+// Wave 0: scan buckets 255..0 (descending keys) for the first bucket where
+// above + (mass of this and higher buckets) >= need; refine the state.
+__device__ void pick_bucket(SelectShared& sh, int shift) {
+  const int lane = threadIdx.x & 63;
+  // lane l owns buckets 255-4l .. 252-4l, highest first
+  uint64_t m[4];
+  uint64_t local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = sh.mass[255 - 4 * lane - i];
+    local += m[i];
+  }
+  uint64_t incl = local;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off);
+    const uint64_t y = __shfl_up(incl, off);
     if (lane >= off) incl += y;
   }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double acc = 0.0;
-    for (int w = 0; w < kSelectWaves; ++w) {
-      const double t = wave_tot[w];
-      wave_tot[w] = acc;
-      acc += t;
-    }
-    wave_tot[kSelectWaves] = acc;
+  const uint64_t before = sh.above + (incl - local);  // mass of buckets above this lane's first
+  const uint64_t need = (uint64_t)sh.need;
+  const bool crosses = before + local >= need;
+  const uint64_t ballot = __ballot(crosses);
+  if (ballot == 0) {  // the candidates never reach R (only possible on the first pass)
+    if (lane == 0) sh.all_optional = 1;
+    return;
   }
-  __syncthreads();
-  const double excl = wave_tot[wave] + (incl - x);
-  *total = wave_tot[kSelectWaves];
-  return excl;
+  const int first = __ffsll((unsigned long long)ballot) - 1;
+  if (lane == first) {
+    uint64_t acc = before;
+    int i = 0;
+    for (; i < 3; ++i) {
+      if (acc + m[i] >= need) break;
+      acc += m[i];
+    }
+    const uint32_t digit = (uint32_t)(255 - 4 * lane - i);
+    sh.prefix |= digit << shift;
+    sh.above = acc;
+    if (shift == 0) {
+      const uint32_t c = sh.cnt[digit];
+      sh.tie_mass = c ? m[i] / c : 0;
+      const uint64_t rest = need - acc;  // > 0, <= m[i]
+      sh.tie_keep = sh.tie_mass ? (rest + sh.tie_mass - 1) / sh.tie_mass : c;
+    }
+  }
 }
 
 __global__ void __launch_bounds__(kSelectThreads) up_select_kernel(SelectArgs a) {
-  extern __shared__ uint64_t keys[];
-  __shared__ double wave_tot[kSelectWaves + 1];
-  __shared__ int wave_kept[kSelectWaves];
-
+  __shared__ SelectShared sh;
   const int req = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s0 = a.cu_seqlens[req];
   const int L = a.cu_seqlens[req + 1] - s0;
   const int cb0 = a.cu_blocks[req];
@@ -84,66 +165,104 @@ __global__ void __launch_bounds__(kSelectThreads) up_select_kernel(SelectArgs a)
     return;
   }
   const int G = a.block;
-  int np = 1;
-  while (np < nb) np <<= 1;
+  const float* sc = a.scores + cb0;
 
-  for (int i = tid; i < np; i += kSelectThreads) {
-    uint64_t key = 0;
-    if (i < nb) {
-      const uint32_t hi =
-          is_forced(i, L, G, a.sink, a.tail) ? 0xFFFFFFFFu : orderable(a.scores[cb0 + i]);
-      key = ((uint64_t)hi << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-    }
-    keys[i] = key;
+  // 1. fixed-point scale from the request's largest score
+  float mx = 0.f;
+  for (int i = tid; i < nb; i += kSelectThreads) mx = fmaxf(mx, sc[i]);
+  mx = block_max(mx, sh);
+  int lg = 0;
+  while ((1ll << lg) < (int64_t)nb + 1) ++lg;
+  const int S = 62 - lg;
+  const double scale = mx > 0.f ? ldexp(1.0, S) / (double)mx : 0.0;
+
+  // 2. total and forced mass
+  uint64_t tot = 0, forced = 0;
+  for (int i = tid; i < nb; i += kSelectThreads) {
+    const uint64_t m = mass_of(sc[i], scale);
+    tot += m;
+    if (is_forced(i, L, G, a.sink, a.tail)) forced += m;
+  }
+  tot = block_sum_u64(tot, sh);
+  forced = block_sum_u64(forced, sh);
+  if (tid == 0) {
+    const uint64_t target = (uint64_t)ceil(a.top_p * (double)tot);
+    sh.need = (int64_t)target - (int64_t)forced;
+    sh.prefix = 0;
+    sh.above = 0;
+    sh.all_optional = 0;
+    sh.tie_mass = 0;
+    sh.tie_keep = 0;
   }
   __syncthreads();
+  const bool any_optional = sh.need > 0;
 
-  // Bitonic sort, descending.
-  for (int k = 2; k <= np; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < np; i += kSelectThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = keys[i], y = keys[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
+  // 3. radix select of the cutoff key over optional blocks, MSB digit first
+  if (any_optional) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int d = tid; d < 256; d += kSelectThreads) {
+        sh.cnt[d] = 0;
+        sh.mass[d] = 0;
       }
       __syncthreads();
+      const uint32_t hi_mask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      const uint32_t prefix = sh.prefix;
+      for (int i = tid; i < nb; i += kSelectThreads) {
+        if (is_forced(i, L, G, a.sink, a.tail)) continue;
+        const float s = sc[i];
+        const uint32_t key = orderable(s);
+        if ((key & hi_mask) != (prefix & hi_mask)) continue;
+        const uint32_t d = (key >> shift) & 0xFFu;
+        atomicAdd(&sh.cnt[d], 1u);
+        atomicAdd((unsigned long long*)&sh.mass[d], (unsigned long long)mass_of(s, scale));
+      }
+      __syncthreads();
+      if (wave == 0) pick_bucket(sh, shift);
+      __syncthreads();
+      if (sh.all_optional) break;
     }
   }
 
-  // Each thread owns a contiguous run of sorted positions.
-  const int per = (np + kSelectThreads - 1) / kSelectThreads;
-  const int p0 = tid * per, p1 = min(p0 + per, nb);
-  double local = 0.0;
-  for (int p = p0; p < p1; ++p) {
-    const int idx = (int)(0xFFFFFFFFu - (uint32_t)(keys[p] & 0xFFFFFFFFu));
-    local += (double)a.scores[cb0 + idx];
-  }
-  double total;
-  double excl = block_exclusive_scan(local, wave_tot, &total);
-  const double target = a.top_p * total;
-
+  // 4. mask: forced, above the cutoff, or among the first tie_keep ties
+  const uint32_t vstar = sh.prefix;
+  const bool keep_all = sh.all_optional != 0;
+  const uint64_t tie_keep = sh.tie_keep;
   int kept_tokens = 0;
-  for (int p = p0; p < p1; ++p) {
-    const int idx = (int)(0xFFFFFFFFu - (uint32_t)(keys[p] & 0xFFFFFFFFu));
-    const bool forced = is_forced(idx, L, G, a.sink, a.tail);
-    const bool keep = forced || (excl < target);
-    a.mask[cb0 + idx] = keep ? 1 : 0;
-    if (keep) kept_tokens += min(idx * G + G, L) - idx * G;
-    excl += (double)a.scores[cb0 + idx];
+  uint64_t ties_before = 0;  // ties at lower indices in earlier rounds
+  for (int base = 0; base < nb; base += kSelectThreads) {
+    const int i = base + tid;
+    bool keep = false, tie = false;
+    if (i < nb) {
+      const bool f = is_forced(i, L, G, a.sink, a.tail);
+      const uint32_t key = orderable(sc[i]);
+      tie = any_optional && !keep_all && !f && key == vstar;
+      keep = f || (any_optional && (keep_all || key > vstar));
+    }
+    // rank of this tie among ties in index order
+    const uint64_t bal = __ballot(tie);
+    const int below_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+    __syncthreads();
+    if (lane == 0) sh.redi[wave] = __popcll(bal);
+    __syncthreads();
+    int below_waves = 0, round_ties = 0;
+    for (int w = 0; w < kSelectWaves; ++w) {
+      if (w < wave) below_waves += sh.redi[w];
+      round_ties += sh.redi[w];
+    }
+    if (tie) keep = (ties_before + below_waves + below_in_wave) < tie_keep;
+    ties_before += round_ties;
+    if (i < nb) {
+      a.mask[cb0 + i] = keep ? 1 : 0;
+      if (keep) kept_tokens += min(i * G + G, L) - i * G;
+    }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) kept_tokens += __shfl_xor(kept_tokens, off);
-  if ((tid & 63) == 0) wave_kept[tid >> 6] = kept_tokens;
+  kept_tokens = wave_sum(kept_tokens);
+  __syncthreads();
+  if (lane == 0) sh.redi[wave] = kept_tokens;
   __syncthreads();
   if (tid == 0) {
     int s = 0;
-    for (int w = 0; w < kSelectWaves; ++w) s += wave_kept[w];
+    for (int w = 0; w < kSelectWaves; ++w) s += sh.redi[w];
     a.kept[req] = s;
   }
 }
@@ -169,24 +288,13 @@ extern "C" up_status up_select_topp(int num_seqs, const int32_t* cu_seqlens_h,
     return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
   const int64_t max_nb = up::ceil_div(max_len, block);
   if (max_nb > up::kMaxBlocksPerRequest)
-    return up::set_error(UP_ERR_UNSUPPORTED, "%lld blocks in one request > %d",
-                         (long long)max_nb, up::kMaxBlocksPerRequest);
+    return up::set_error(UP_ERR_UNSUPPORTED, "%lld blocks in one request > %lld",
+                         (long long)max_nb, (long long)up::kMaxBlocksPerRequest);
   st = up::check_device();
   if (st != UP_OK) return st;
-  int np = 1;
-  while (np < max_nb) np <<= 1;
-  const size_t lds = (size_t)np * sizeof(uint64_t);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(up::up_select_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(up::kMaxBlocksPerRequest * sizeof(uint64_t)));
-    (void)hipGetLastError();
-    attr_set = true;
-  }
   up::SelectArgs a{cu_seqlens_d, cu_blocks_d, block_scores, block_mask, kept_tokens,
                    block, sink, tail, top_p};
-  hipLaunchKernelGGL(up::up_select_kernel, dim3((unsigned)num_seqs), dim3(up::kSelectThreads), lds,
+  hipLaunchKernelGGL(up::up_select_kernel, dim3((unsigned)num_seqs), dim3(up::kSelectThreads), 0,
                      stream, a);
   return up::check_launch("up_select_kernel");
 }
