@@ -29,9 +29,9 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Geometry of the scoring kernels for one call (computed on the host).
 struct ScoreGeometry {
-  int rows_per_wg;   // query rows one workgroup holds in registers
-  int waves;         // waves per workgroup
-  int rg;            // row groups per KV head
+  int rows_per_wg;   // query rows one column-sum workgroup holds in registers
+  int rg;            // column-sum row groups per KV head
+  int rg_a;          // row-statistics row groups per KV head
   int ck;            // keys per workgroup chunk
   int max_chunks;    // chunks of the longest request
   size_t off_partial, off_bias, off_colpart, bytes;

@@ -31,7 +31,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int KT = 64;  // keys per LDS tile (two 32-wide MFMA tiles)
+// Keys per LDS tile: two 32-wide MFMA tiles, one for head_dim 256 so that a
+// four-tile ring stays at 64 KiB of LDS.
+template <int D> struct KeysPerTile { static constexpr int value = D >= 256 ? 32 : 64; };
+constexpr int kRing = 4;  // LDS tiles per ring: two resident + two in flight
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
@@ -91,37 +94,85 @@ __device__ __forceinline__ Work decode_work(const ScoreArgs& a) {
   return wk;
 }
 
-// Key rows of one tile: global -> registers -> LDS (double-buffered by caller).
+// Key rows of one LDS tile, fetched with direct global->LDS loads
+// (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at base + 16 i),
+// so no registers stage the tile.  Rows are D*2 bytes, unpadded; the 16-byte
+// chunk c of tile row r sits in slot c ^ (r & SWZ), which spreads the rows a
+// fragment read touches over all LDS banks.
 template <int D, int W>
 struct KTile {
-  static constexpr int VPR = D / 8;                  // 16-byte vectors per key row
-  static constexpr int VPT = KT * VPR / (64 * W);    // vectors per thread
-  static constexpr int STRIDE = D + 8;               // LDS row stride, elements
-  static_assert(KT * VPR % (64 * W) == 0, "tile not divisible among threads");
-  u32x4_t r[VPT];
+  static constexpr int KT = KeysPerTile<D>::value;
+  static constexpr int CHUNKS = D / 8;                  // 16-byte chunks per key row
+  static constexpr int RPI = 64 / CHUNKS;               // rows one wave instruction fills
+  static constexpr int INSTS = KT / RPI / W;            // load instructions per wave per tile
+  static constexpr int SWZ = CHUNKS < 16 ? CHUNKS - 1 : 15;
+  static constexpr int ELEMS = KT * D;                  // elements per tile
+  static_assert(KT % (RPI * W) == 0, "tile not divisible among waves");
 
-  __device__ __forceinline__ void load(const uint16_t* kbase, int64_t k_tok, int tkey0,
-                                       int key_end, int tid) {
+  // Fetch keys [tkey0, tkey0 + KT) into `lds`; keys >= key_end read the last
+  // valid key instead (in bounds; the masked path ignores them).
+  static __device__ __forceinline__ void fetch(const uint16_t* kbase, int64_t k_tok, int tkey0,
+                                               int key_end, uint16_t* lds, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int e = i * 64 * W + tid;
-      const int row = e / VPR, col = e % VPR;
-      const int key = tkey0 + row;
-      if (key < key_end)
-        r[i] = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)key * k_tok + col * 8);
-      else
-        r[i] = (u32x4_t){0u, 0u, 0u, 0u};
+    for (int i = 0; i < INSTS; ++i) {
+      const int j = wave * INSTS + i;
+      const int r = j * RPI + lane / CHUNKS;
+      const int c = (lane % CHUNKS) ^ (r & SWZ);
+      const int key = min(tkey0 + r, key_end - 1);
+      __builtin_amdgcn_global_load_lds(kbase + (int64_t)key * k_tok + c * 8, lds + j * RPI * D, 16,
+                                       0, 0);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int e = i * 64 * W + tid;
-      const int row = e / VPR, col = e % VPR;
-      *reinterpret_cast<u32x4_t*>(lds + row * STRIDE + col * 8) = r[i];
-    }
-  }
+  // Element offset of chunk c of tile row r.
+  static __device__ __forceinline__ int offset(int r, int c) { return r * D + ((c ^ (r & SWZ)) << 3); }
 };
+
+// Workgroup barrier that waits only for this wave's LDS operations; the K
+// tile fetches in flight are covered by an explicit wait_vmcnt before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+// Ring start: fetch tiles 0..2 (as many as exist), wait for tiles 0 and 1.
+template <typename Tile>
+__device__ __forceinline__ void ring_prologue(const uint16_t* kbase, int64_t k_tok, int key0,
+                                              int key1, int ntiles, uint16_t (*kl)[Tile::ELEMS],
+                                              int wave, int lane);
+// Ring step: tile it+2 must be resident for the next iteration; tile it+3
+// (fetched this iteration when `more`) may stay in flight.
+template <typename Tile>
+__device__ __forceinline__ void ring_advance(bool more);
+
+// Wait until at most N of this wave's vector-memory loads (the K tile
+// fetches) are in flight.  Written as an asm statement so the compiler's own
+// wait-count pass keeps it exactly as placed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <typename Tile>
+__device__ __forceinline__ void ring_prologue(const uint16_t* kbase, int64_t k_tok, int key0,
+                                              int key1, int ntiles, uint16_t (*kl)[Tile::ELEMS],
+                                              int wave, int lane) {
+  Tile::fetch(kbase, k_tok, key0, key1, kl[0], wave, lane);
+  if (ntiles > 1) Tile::fetch(kbase, k_tok, key0 + Tile::KT, key1, kl[1], wave, lane);
+  if (ntiles > 2) {
+    Tile::fetch(kbase, k_tok, key0 + 2 * Tile::KT, key1, kl[2], wave, lane);
+    wait_vmcnt<Tile::INSTS>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+}
+
+template <typename Tile>
+__device__ __forceinline__ void ring_advance(bool more) {
+  if (more) wait_vmcnt<Tile::INSTS>(); else wait_vmcnt<0>();
+  lds_barrier();
+}
 
 // Query fragments of the lane's rows.  Row rho of KV group g is query head
 // g*rgqa + rho/n_eff at tail position rho%n_eff.  The same registers serve as
@@ -151,12 +202,126 @@ __device__ __forceinline__ void load_q(const ScoreArgs& a, int s0, int qpos0, in
 }
 
 // ---------------------------------------------------------------------------
-// Pass A: per-row running max and sum of exp2 over one key chunk.
+// Shared pieces of the two passes.
+//
+// Both passes walk the chunk's keys in LDS tiles of KT keys held in a
+// four-buffer ring: when iteration it starts, tiles it and it+1 are resident
+// and tile it+2 is in flight; iteration it fetches tile it+3.  Both passes
+// may software-pipeline over "groups": one
+// group is one 32x32 S tile (32 keys x 32 query rows).  While the VALU works
+// on group g (scale, exp2, reductions), the MFMAs of group g+1 are already
+// issued, so the matrix cores and the VALU run side by side within a wave.
 // ---------------------------------------------------------------------------
-template <int D, int NT, int W>
-__global__ void __launch_bounds__(64 * W) up_rowstats_kernel(ScoreArgs a) {
+
+// Sum of 16 values as a balanced tree (short dependency chains).
+__device__ __forceinline__ float tree_sum16(const float (&e)[16]) {
+  float a0 = (e[0] + e[1]) + (e[2] + e[3]), a1 = (e[4] + e[5]) + (e[6] + e[7]);
+  float a2 = (e[8] + e[9]) + (e[10] + e[11]), a3 = (e[12] + e[13]) + (e[14] + e[15]);
+  return (a0 + a1) + (a2 + a3);
+}
+
+// Interleave hint for one group: one MFMA then a few VALU ops, D/16 times.
+template <int D>
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x402, 64 / (D / 16), 0);    // VALU or TRANS
+  }
+}
+
+template <int D, int W>
+__device__ __forceinline__ void load_frags(const uint16_t* tile, int sub, int lane,
+                                           bf16x8_t (&f)[D / 16]) {
   using Tile = KTile<D, W>;
-  __shared__ __attribute__((aligned(16))) uint16_t kl[2][KT * Tile::STRIDE];
+  const int r = sub * 32 + (lane & 31);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) f[s] = load_bf16x8(tile + Tile::offset(r, 2 * s + (lane >> 5)));
+}
+
+// ---------------------------------------------------------------------------
+// Pass A: per-row running max and sum of exp2 over one key chunk.
+// Keys on the MFMA M axis (A operand from LDS), query rows on N (B operand
+// from registers): lane l owns row (l % 32), 16 keys per S tile.
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ void rowstats_update(f32x16_t acc, int t, bool masked, int mkey0,
+                                                int key1, int lane, float C,
+                                                const int (&ipos)[NT], float (&m_run)[NT],
+                                                float (&l_run)[NT]) {
+  float x[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = acc[v];
+  if (masked) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = mkey0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (j >= key1 || j > ipos[t]) x[v] = kNegInf;
+    }
+  }
+  float mx = fmaxf(fmaxf(x[0], x[1]), m_run[t]);
+#pragma unroll
+  for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, x[v]), x[v + 1]);
+  const float mc = (mx == kNegInf) ? 0.f : mx * C;
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(x[v], C, -mc));
+  l_run[t] = fmaf(l_run[t], fast_exp2(fmaf(m_run[t], C, -mc)), tree_sum16(e));
+  m_run[t] = mx;
+}
+
+// One LDS tile: NG = (KT/32)*NT groups, ordered (mt, t).  On entry acc holds
+// the (issued) S of group 0 of this tile and af the A fragments of mt = 0;
+// on exit they hold group 0 of the next tile (from `nxt`).
+template <int D, int NT, int W, bool MASKED, bool PIPE>
+__device__ __forceinline__ void rowstats_iter(const uint16_t* cur, const uint16_t* nxt, int tkey0,
+                                              int key1, int lane, float C,
+                                              const bf16x8_t (&qf)[NT][D / 16],
+                                              const int (&ipos)[NT], float (&m_run)[NT],
+                                              float (&l_run)[NT], f32x16_t& acc,
+                                              bf16x8_t (&af)[D / 16]) {
+  constexpr int KT = KTile<D, W>::KT;
+  constexpr int NG = (KT / 32) * NT;
+  if constexpr (!PIPE) {
+#pragma unroll
+    for (int mt = 0; mt < KT / 32; ++mt) {
+      load_frags<D, W>(cur, mt, lane, af);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x16_t sacc = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) sacc = mfma32(af[s], qf[t][s], sacc);
+        rowstats_update<NT>(sacc, t, MASKED, tkey0 + mt * 32, key1, lane, C, ipos, m_run, l_run);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int mt = q / NT, t = q % NT;
+    f32x16_t nacc = {};
+    if (q + 1 < NG) {
+      const int mt1 = (q + 1) / NT, t1 = (q + 1) % NT;
+      if (mt1 != mt) load_frags<D, W>(cur, mt1, lane, af);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) nacc = mfma32(af[s], qf[t1][s], nacc);
+    } else {
+      load_frags<D, W>(nxt, 0, lane, af);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) nacc = mfma32(af[s], qf[0][s], nacc);
+    }
+    rowstats_update<NT>(acc, t, MASKED, tkey0 + mt * 32, key1, lane, C, ipos, m_run, l_run);
+    acc = nacc;
+    if (PIPE) interleave_hint<D>();
+  }
+}
+
+template <int D, int NT, int W, bool PIPE>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+up_rowstats_kernel(ScoreArgs a) {
+  using Tile = KTile<D, W>;
+  constexpr int KT = Tile::KT;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[kRing][Tile::ELEMS];
 
   const Work wk = decode_work(a);
   if (!wk.valid) return;
@@ -187,50 +352,32 @@ __global__ void __launch_bounds__(64 * W) up_rowstats_kernel(ScoreArgs a) {
 
   const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
   const int ntiles = (key1 - key0 + KT - 1) / KT;
-  Tile tile;
-  tile.load(kbase, a.k_tok, key0, key1, tid);
-  tile.store(kl[0], tid);
-  __syncthreads();
+  // leading tiles that need no mask: every key < key1 and <= every tail row
+  const int lim = min(key1, qpos0 + 1);
+  const int nfast = lim > key0 ? (lim - key0) / KT : 0;
+  ring_prologue<Tile>(kbase, a.k_tok, key0, key1, ntiles, kl, wave, lane);
+
+  bf16x8_t af[D / 16];
+  f32x16_t acc = {};
+  if constexpr (PIPE) {
+    load_frags<D, W>(kl[0], 0, lane, af);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) acc = mfma32(af[s], qf[0][s], acc);
+  }
 
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+    const uint16_t* cur = kl[it % kRing];
+    const uint16_t* nxt = kl[(it + 1) % kRing];
     const int tkey0 = key0 + it * KT;
-    if (it + 1 < ntiles) tile.load(kbase, a.k_tok, tkey0 + KT, key1, tid);
-
-#pragma unroll
-    for (int mt = 0; mt < KT / 32; ++mt) {
-      bf16x8_t af[D / 16];
-      const uint16_t* lrow = kl[buf] + (mt * 32 + (lane & 31)) * Tile::STRIDE + (lane >> 5) * 8;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) af[s] = load_bf16x8(lrow + s * 16);
-      const int mkey0 = tkey0 + mt * 32;
-      const bool need_mask = (mkey0 + 31 > qpos0) || (mkey0 + 31 >= key1);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f32x16_t acc = {};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) acc = mfma32(af[s], qf[t][s], acc);
-        if (need_mask) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int j = mkey0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (j >= key1 || j > ipos[t]) acc[v] = kNegInf;
-          }
-        }
-        float mx = acc[0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
-        const float mnew = fmaxf(m_run[t], mx);
-        const float mc = (mnew == kNegInf) ? 0.f : mnew * C;
-        float sum = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sum += fast_exp2(fmaf(acc[v], C, -mc));
-        l_run[t] = fmaf(l_run[t], fast_exp2(fmaf(m_run[t], C, -mc)), sum);
-        m_run[t] = mnew;
-      }
-    }
-    if (it + 1 < ntiles) tile.store(kl[buf ^ 1], tid);
-    __syncthreads();
+    const bool more = it + 3 < ntiles;
+    if (more) Tile::fetch(kbase, a.k_tok, tkey0 + 3 * KT, key1, kl[(it + 3) % kRing], wave, lane);
+    if (it < nfast)
+      rowstats_iter<D, NT, W, false, PIPE>(cur, nxt, tkey0, key1, lane, C, qf, ipos, m_run, l_run,
+                                           acc, af);
+    else
+      rowstats_iter<D, NT, W, true, PIPE>(cur, nxt, tkey0, key1, lane, C, qf, ipos, m_run, l_run,
+                                          acc, af);
+    ring_advance<Tile>(more);
   }
 
   // Merge the two half-waves (same row, disjoint keys) and write the partial.
@@ -279,12 +426,95 @@ __global__ void __launch_bounds__(256) up_rowstats_combine_kernel(ScoreArgs a) {
 
 // ---------------------------------------------------------------------------
 // Pass B: column sums of the normalised probabilities over the chunk's keys.
+// Query rows on the MFMA M axis (A operand from registers), keys on N
+// (B operand from LDS): lane l owns key (l % 32), 16 rows per S tile.
 // ---------------------------------------------------------------------------
-template <int D, int NT, int W>
-__global__ void __launch_bounds__(64 * W) up_colsum_kernel(ScoreArgs a) {
+template <int NT>
+__device__ __forceinline__ float colsum_update(f32x16_t acc, int t, bool masked, int key, int key1,
+                                               int lane, int row0, int R, int n_eff, int qpos0,
+                                               float C, const float (&bv)[NT][16]) {
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], C, -bv[t][v]));
+  if (masked) {
+    // Rebuilt on every masked tile from an opaque base, so the compiler does
+    // not keep 16*NT row positions alive across the whole key loop.
+    int base;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(base) : "v"(row0 + t * 32 + 4 * (lane >> 5)));
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rho = base + 8 * (v >> 2) + (v & 3);
+      const int ti = rho < R ? rho % n_eff : 0;
+      if (!((key < key1) && (key <= qpos0 + ti))) e[v] = 0.f;
+    }
+  }
+  return tree_sum16(e);
+}
+
+// One LDS tile: NG = (KT/32)*NT groups ordered (nt, t); the column sum of
+// key sub-tile nt is complete after its last t and goes to LDS.
+template <int D, int NT, int W, bool MASKED, bool PIPE>
+__device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t* nxt, int tkey0,
+                                            int key1, int lane, int wave, int row0, int R,
+                                            int n_eff, int qpos0, float C,
+                                            const bf16x8_t (&qf)[NT][D / 16],
+                                            const float (&bv)[NT][16], float (*colrow)[64],
+                                            f32x16_t& acc, bf16x8_t (&kf)[D / 16]) {
+  constexpr int KT = KTile<D, W>::KT;
+  constexpr int NG = (KT / 32) * NT;
+  float col = 0.f;
+  if constexpr (!PIPE) {
+    // Straight order: each group's MFMAs, then its VALU work.
+#pragma unroll
+    for (int nt = 0; nt < KT / 32; ++nt) {
+      load_frags<D, W>(cur, nt, lane, kf);
+      const int key = tkey0 + nt * 32 + (lane & 31);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x16_t sacc = {};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) sacc = mfma32(qf[t][s], kf[s], sacc);
+        col += colsum_update<NT>(sacc, t, MASKED, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
+      }
+      col += __shfl_xor(col, 32);
+      if (lane < 32) colrow[wave][nt * 32 + lane] = col;
+      col = 0.f;
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int nt = q / NT, t = q % NT;
+    f32x16_t nacc = {};
+    if (q + 1 < NG) {
+      const int nt1 = (q + 1) / NT, t1 = (q + 1) % NT;
+      if (nt1 != nt) load_frags<D, W>(cur, nt1, lane, kf);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) nacc = mfma32(qf[t1][s], kf[s], nacc);
+    } else {
+      load_frags<D, W>(nxt, 0, lane, kf);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) nacc = mfma32(qf[0][s], kf[s], nacc);
+    }
+    const int key = tkey0 + nt * 32 + (lane & 31);
+    col += colsum_update<NT>(acc, t, MASKED, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
+    if (t == NT - 1) {
+      col += __shfl_xor(col, 32);
+      if (lane < 32) colrow[wave][nt * 32 + lane] = col;
+      col = 0.f;
+    }
+    acc = nacc;
+    if (PIPE) interleave_hint<D>();
+  }
+}
+
+template <int D, int NT, int W, bool PIPE>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+up_colsum_kernel(ScoreArgs a) {
   using Tile = KTile<D, W>;
-  __shared__ __attribute__((aligned(16))) uint16_t kl[2][KT * Tile::STRIDE];
-  __shared__ float colbuf[2][W][KT];
+  constexpr int KT = Tile::KT;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[kRing][Tile::ELEMS];
+  __shared__ float colbuf[2][W][64];
 
   const Work wk = decode_work(a);
   if (!wk.valid) return;
@@ -325,55 +555,39 @@ __global__ void __launch_bounds__(64 * W) up_colsum_kernel(ScoreArgs a) {
   const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
   float* colout = a.colpart + ((int64_t)g * a.rg + rgi) * a.T + s0;
   const int ntiles = (key1 - key0 + KT - 1) / KT;
-  Tile tile;
-  tile.load(kbase, a.k_tok, key0, key1, tid);
-  tile.store(kl[0], tid);
-  __syncthreads();
+  const int lim = min(key1, qpos0 + 1);
+  const int nfast = lim > key0 ? (lim - key0) / KT : 0;
+  ring_prologue<Tile>(kbase, a.k_tok, key0, key1, ntiles, kl, wave, lane);
+
+  bf16x8_t kf[D / 16];
+  f32x16_t acc = {};
+  if constexpr (PIPE) {
+    load_frags<D, W>(kl[0], 0, lane, kf);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) acc = mfma32(qf[0][s], kf[s], acc);
+  }
 
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+    const int cb = it & 1;
+    const uint16_t* cur = kl[it % kRing];
+    const uint16_t* nxt = kl[(it + 1) % kRing];
     const int tkey0 = key0 + it * KT;
-    if (it + 1 < ntiles) tile.load(kbase, a.k_tok, tkey0 + KT, key1, tid);
-
-#pragma unroll
-    for (int nt = 0; nt < KT / 32; ++nt) {
-      bf16x8_t kf[D / 16];
-      const uint16_t* lrow = kl[buf] + (nt * 32 + (lane & 31)) * Tile::STRIDE + (lane >> 5) * 8;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) kf[s] = load_bf16x8(lrow + s * 16);
-      const int key = tkey0 + nt * 32 + (lane & 31);
-      const bool need_mask = (tkey0 + nt * 32 + 31 > qpos0) || (tkey0 + nt * 32 + 31 >= key1);
-      float col = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f32x16_t acc = {};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) acc = mfma32(qf[t][s], kf[s], acc);
-        if (!need_mask) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) col += fast_exp2(fmaf(acc[v], C, -bv[t][v]));
-        } else {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rho = row0 + t * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            const int ti = rho < R ? rho % n_eff : 0;
-            const bool ok = (key < key1) && (key <= qpos0 + ti);
-            col += ok ? fast_exp2(fmaf(acc[v], C, -bv[t][v])) : 0.f;
-          }
-        }
-      }
-      col += __shfl_xor(col, 32);
-      if (lane < 32) colbuf[buf][wave][nt * 32 + lane] = col;
-    }
-    if (it + 1 < ntiles) tile.store(kl[buf ^ 1], tid);
-    __syncthreads();
+    const bool more = it + 3 < ntiles;
+    if (more) Tile::fetch(kbase, a.k_tok, tkey0 + 3 * KT, key1, kl[(it + 3) % kRing], wave, lane);
+    if (it < nfast)
+      colsum_iter<D, NT, W, false, PIPE>(cur, nxt, tkey0, key1, lane, wave, row0, R, n_eff, qpos0, C,
+                                         qf, bv, colbuf[cb], acc, kf);
+    else
+      colsum_iter<D, NT, W, true, PIPE>(cur, nxt, tkey0, key1, lane, wave, row0, R, n_eff, qpos0, C,
+                                        qf, bv, colbuf[cb], acc, kf);
+    ring_advance<Tile>(more);
     if (tid < KT) {
       const int key = tkey0 + tid;
       if (key < key1) {
-        float s = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < W; ++w) s += colbuf[buf][w][tid];
-        colout[key] = s;
+        for (int w = 0; w < W; ++w) sum += colbuf[cb][w][tid];
+        colout[key] = sum;
       }
     }
   }
@@ -415,32 +629,54 @@ __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
   if (lane == 0) a.block_scores[b] = sum / (float)(j1 - j0);
 }
 
-// Compile-time tiling per head_dim: NT 32-row tiles per wave, W waves.
+// Compile-time tiling per head_dim and pass: NT 32-row tiles per wave, W
+// waves per workgroup, PIPE = software-pipelined MFMA/VALU interleave.  Pass A
+// writes per-row partials, so the two passes may group rows differently.
+#ifndef UP_TILE_A128
+#define UP_TILE_A128 2, 4, true
+#endif
+#ifndef UP_TILE_B128
+#define UP_TILE_B128 2, 8, false
+#endif
+template <int NT_, int W_, bool PIPE_>
+struct TileCfg {
+  static constexpr int NT = NT_, W = W_;
+  static constexpr bool PIPE = PIPE_;
+  static constexpr int ROWS = NT * 32 * W;
+};
 template <int D> struct Tiling;
-template <> struct Tiling<64> { static constexpr int NT = 2, W = 8; };
-template <> struct Tiling<128> { static constexpr int NT = 2, W = 8; };
-template <> struct Tiling<256> { static constexpr int NT = 1, W = 8; };
+template <> struct Tiling<64> { using A = TileCfg<2, 4, true>; using B = TileCfg<2, 4, false>; };
+template <> struct Tiling<128> { using A = TileCfg<UP_TILE_A128>; using B = TileCfg<UP_TILE_B128>; };
+template <> struct Tiling<256> { using A = TileCfg<1, 4, true>; using B = TileCfg<1, 4, false>; };
 
-int rows_per_wg_for(int d) {
+int rows_per_wg_for(int d, bool pass_b) {
   switch (d) {
-    case 64: return Tiling<64>::NT * 32 * Tiling<64>::W;
-    case 128: return Tiling<128>::NT * 32 * Tiling<128>::W;
-    default: return Tiling<256>::NT * 32 * Tiling<256>::W;
+    case 64: return pass_b ? Tiling<64>::B::ROWS : Tiling<64>::A::ROWS;
+    case 128: return pass_b ? Tiling<128>::B::ROWS : Tiling<128>::A::ROWS;
+    default: return pass_b ? Tiling<256>::B::ROWS : Tiling<256>::A::ROWS;
   }
 }
 
+int64_t grid_for(const ScoreArgs& a) { return ceil_div(a.num_groups, 8) * 8 * a.rg; }
+
 template <int D>
-up_status launch_passes(const ScoreArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int NT = Tiling<D>::NT, W = Tiling<D>::W;
-  hipLaunchKernelGGL((up_rowstats_kernel<D, NT, W>), grid, dim3(64 * W), 0, st, a);
+up_status launch_passes(const ScoreArgs& b_args, int rg_a, hipStream_t st) {
+  using TA = typename Tiling<D>::A;
+  using TB = typename Tiling<D>::B;
+  ScoreArgs aa = b_args;
+  aa.rg = rg_a;
+  aa.rows_per_wg = TA::ROWS;
+  hipLaunchKernelGGL((up_rowstats_kernel<D, TA::NT, TA::W, TA::PIPE>), dim3((unsigned)grid_for(aa)),
+                     dim3(64 * TA::W), 0, st, aa);
   up_status s = check_launch("up_rowstats_kernel");
   if (s != UP_OK) return s;
-  const int64_t rows = (int64_t)a.num_seqs * a.hq * a.n_query;
+  const int64_t rows = (int64_t)b_args.num_seqs * b_args.hq * b_args.n_query;
   hipLaunchKernelGGL(up_rowstats_combine_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0,
-                     st, a);
+                     st, b_args);
   s = check_launch("up_rowstats_combine_kernel");
   if (s != UP_OK) return s;
-  hipLaunchKernelGGL((up_colsum_kernel<D, NT, W>), grid, dim3(64 * W), 0, st, a);
+  hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE>),
+                     dim3((unsigned)grid_for(b_args)), dim3(64 * TB::W), 0, st, b_args);
   return check_launch("up_colsum_kernel");
 }
 
@@ -449,10 +685,12 @@ up_status launch_passes(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv, int head_dim,
                              int n_query) {
   ScoreGeometry g{};
-  g.rows_per_wg = rows_per_wg_for(head_dim);
   const int rgqa = hkv > 0 ? hq / hkv : 1;
   const int64_t rmax = (int64_t)rgqa * (n_query < max_len ? n_query : max_len);
+  g.rows_per_wg = rows_per_wg_for(head_dim, true);
   g.rg = (int)(rmax > 0 ? ceil_div(rmax, g.rows_per_wg) : 1);
+  const int rows_a = rows_per_wg_for(head_dim, false);
+  g.rg_a = (int)(rmax > 0 ? ceil_div(rmax, rows_a) : 1);
   g.ck = 0;  // chosen by the caller once lengths are known
   g.max_chunks = 0;
   (void)num_seqs;
@@ -500,7 +738,7 @@ up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int h
   if (n_query < 1 || n_query > 4096)
     return up::set_error(UP_ERR_UNSUPPORTED, "n_query %d not in [1, 4096]", n_query);
   up::ScoreGeometry g = up::score_geometry(num_seqs, T, max_len, hq, hkv, head_dim, n_query);
-  g.ck = choose_ck(num_seqs, cu_h, hkv, g.rg);
+  g.ck = choose_ck(num_seqs, cu_h, hkv, g.rg > g.rg_a ? g.rg : g.rg_a);
   g.max_chunks = (int)(max_len > 0 ? up::ceil_div(max_len, g.ck) : 1);
   size_t off = 0;
   g.off_partial = off;
@@ -594,13 +832,12 @@ up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_
   a.num_blocks = N;
 
   a.num_groups = (int64_t)num_seqs * hkv * a.max_chunks;
-  const int64_t nwg = up::ceil_div(a.num_groups, 8) * 8 * a.rg;
+  const int64_t nwg = up::ceil_div(a.num_groups, 8) * 8 * (a.rg > lay.g.rg_a ? a.rg : lay.g.rg_a);
   if (nwg > 0x7fffffff) return up::set_error(UP_ERR_UNSUPPORTED, "grid too large");
-  dim3 grid((unsigned)nwg);
   switch (head_dim) {
-    case 64: st = up::launch_passes<64>(a, grid, stream); break;
-    case 128: st = up::launch_passes<128>(a, grid, stream); break;
-    default: st = up::launch_passes<256>(a, grid, stream); break;
+    case 64: st = up::launch_passes<64>(a, lay.g.rg_a, stream); break;
+    case 128: st = up::launch_passes<128>(a, lay.g.rg_a, stream); break;
+    default: st = up::launch_passes<256>(a, lay.g.rg_a, stream); break;
   }
   if (st != UP_OK) return st;
   if (N > 0) {
