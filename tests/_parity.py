@@ -140,3 +140,17 @@ def check_compaction(run: GpuRun, mask: np.ndarray, kept_gpu=None):
     if kept_gpu is not None:
         assert list(np.diff(cu_out)) == list(kept_gpu)
     return n
+
+
+def oracle_qk(inputs, n_query):
+    """fp64 copies of the inputs the oracle needs: the tail rows of q (all
+    other rows stay zero and are never read) and every row of k."""
+    cu = inputs["cu_seqlens"].numpy()
+    q = inputs["q"]
+    q64 = np.zeros(tuple(q.shape), dtype=np.float64)   # pages never touched stay virtual
+    for r in range(len(cu) - 1):
+        s0, s1 = int(cu[r]), int(cu[r + 1])
+        ne = min(n_query, s1 - s0)
+        if ne:
+            q64[s1 - ne:s1] = bf16_to_f64(q[s1 - ne:s1])
+    return q64, bf16_to_f64(inputs["k"])
