@@ -45,6 +45,11 @@ def parse_args():
                     help="skip the CPU oracle leg (for profiler runs)")
     ap.add_argument("--cpu-threads", type=int, default=1,
                     help="BLAS threads the oracle may use")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (the reference for counter scaling)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-probe run into profiles/traffic.json and exit")
     return ap.parse_args()
 
 
@@ -66,8 +71,58 @@ def load_traffic(kernel: str, src: str, launches_per_call: int = 1):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30
+TRAFFIC_KERNELS = {"up_compact_kernel": "up_compact.hip", "up_rowstats_kernel": "up_score.hip",
+                   "up_colsum_kernel": "up_score.hip", "up_select_kernel": "up_select.hip"}
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> None:
+    """HBM bytes per dispatch of the path's kernels from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the factor that makes the plain copy of
+    COPY_BYTES read and write exactly COPY_BYTES."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    def load(path, counter):
+        per = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            per[name].append(float(r["Counter_Value"]) * 1024.0)
+        return per
+
+    out = {}
+    for counter, path, key in (("FETCH_SIZE", fetch_csv, "fetch"), ("WRITE_SIZE", write_csv, "write")):
+        per = load(path, counter)
+        # the probe is the runtime's device-to-device copy of COPY_BYTES (the
+        # largest such copy in the run); torch's dtype-conversion kernels also
+        # carry "copy" in their names and are not it
+        copies = [max(v) for n, v in per.items() if "copyBuffer" in n]
+        if not copies:
+            raise SystemExit(f"no copy kernel in {path}")
+        scale = COPY_BYTES / max(copies)
+        for short, src in TRAFFIC_KERNELS.items():
+            vals = [x for n, v in per.items() if re.search(r"\b" + short + r"\b", n) for x in v]
+            if not vals:
+                continue
+            rec = out.setdefault(short, {"source_sha": source_sha(src), "source": src})
+            rec[key + "_bytes_per_launch"] = sum(vals) / len(vals) * scale
+            rec[key + "_scale"] = scale
+            rec[key + "_raw_kib_per_launch"] = sum(vals) / len(vals) / 1024.0
+    for rec in out.values():
+        rec["bytes_per_launch"] = rec.get("fetch_bytes_per_launch", 0.0) + rec.get("write_bytes_per_launch", 0.0)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the head-parallel design is described, not built)", file=sys.stderr)
@@ -124,6 +179,12 @@ def main():
     for i in range(args.warmup):
         step(layer=i)
         U.up_history_init(ledger, B, cap)
+    if args.copy_probe:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
     kept = int(ws.cu_seqlens_out[-1].item())
 
