@@ -46,7 +46,7 @@ struct ScoreArgs {
   int64_t q_tok, q_head, k_tok, k_head;
   int num_seqs, hq, hkv, rgqa, n_query, block;
   int ck, max_chunks, rg, rows_per_wg;
-  int64_t num_groups;  // B * hkv * max_chunks (request, KV head, key chunk) groups
+  int64_t num_groups;  // real (request, KV head, key chunk) groups
   float c;  // scale * log2(e)
   float2* partial;  // [B][hq][n_query][max_chunks] (raw max, sum of exp2)
   float* bias;      // [B][hq][n_query]
@@ -67,12 +67,14 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Work decode shared by both passes.  Workgroups that read the same K chunk
-// (the rg row groups of one (request, KV head, chunk) group) get ids that are
-// equal mod 8, so they run on the same XCD (ids are dealt round-robin over the
-// 8 XCDs) and are dispatched close together: their K re-reads hit that XCD's
-// L2.  Consecutive groups on one XCD are consecutive chunks of the same head,
-// which share the query rows.
+// Work decode shared by both passes.  The groups of work are the real
+// (request, KV head, key chunk) triples, numbered densely: request-major,
+// then KV head, then chunk.  Workgroups that read the same K chunk (the rg row
+// groups of one group) get ids that are equal mod 8, so they run on the same
+// XCD (ids are dealt round-robin over the 8 XCDs) and are dispatched close
+// together: their K re-reads hit that XCD's L2.  Consecutive groups are
+// consecutive chunks of one head, so every request's chunks spread evenly
+// over the XCDs whatever the mix of request lengths.
 struct Work {
   int req, g, chunk, rgi;
   bool valid;
@@ -84,13 +86,25 @@ __device__ __forceinline__ Work decode_work(const ScoreArgs& a) {
   const int64_t blk = w / span, rem = w - blk * span;
   Work wk;
   wk.rgi = (int)(rem >> 3);
-  const int64_t q = blk * 8 + (rem & 7);
+  int64_t q = blk * 8 + (rem & 7);
   wk.valid = q < a.num_groups;
-  const int64_t per_req = (int64_t)a.hkv * a.max_chunks;
-  wk.req = (int)(q / per_req);
-  const int64_t r2 = q - (int64_t)wk.req * per_req;
-  wk.g = (int)(r2 / a.max_chunks);
-  wk.chunk = (int)(r2 - (int64_t)wk.g * a.max_chunks);
+  wk.req = 0;
+  wk.g = 0;
+  wk.chunk = 0;
+  if (!wk.valid) return wk;
+  // find the request holding group q (uniform scalar loop over requests)
+  int r = 0;
+  for (; r < a.num_seqs; ++r) {
+    const int L = a.cu_seqlens[r + 1] - a.cu_seqlens[r];
+    const int64_t ng = (int64_t)((L + a.ck - 1) / a.ck) * a.hkv;
+    if (q < ng) break;
+    q -= ng;
+  }
+  const int L = a.cu_seqlens[r + 1] - a.cu_seqlens[r];
+  const int nch = (L + a.ck - 1) / a.ck;
+  wk.req = r;
+  wk.g = (int)(q / nch);
+  wk.chunk = (int)(q - (int64_t)wk.g * nch);
   return wk;
 }
 
@@ -705,15 +719,21 @@ extern "C" up_status up_score_workspace_size(int num_seqs, const int32_t* cu_seq
 
 namespace {
 
-// Key chunk per workgroup: the largest power of two in [256, 4096] that
-// still gives >= 1024 workgroups (four per CU) for this batch.
+#ifndef UP_CK_MAX
+#define UP_CK_MAX 2048
+#endif
+#ifndef UP_MIN_WGS
+#define UP_MIN_WGS 1024
+#endif
+// Key chunk per workgroup: the largest power of two in [256, UP_CK_MAX] that
+// still gives >= UP_MIN_WGS workgroups for this batch.
 int choose_ck(int num_seqs, const int32_t* cu_h, int hkv, int rg) {
-  int ck = 4096;
+  int ck = UP_CK_MAX;
   while (ck > 256) {
     int64_t wgs = 0;
     for (int r = 0; r < num_seqs; ++r)
       wgs += up::ceil_div(cu_h[r + 1] - cu_h[r], ck) * (int64_t)hkv * rg;
-    if (wgs >= 1024) break;
+    if (wgs >= UP_MIN_WGS) break;
     ck >>= 1;
   }
   return ck;
@@ -831,7 +851,9 @@ up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_
   a.block_scores = block_scores;
   a.num_blocks = N;
 
-  a.num_groups = (int64_t)num_seqs * hkv * a.max_chunks;
+  a.num_groups = 0;
+  for (int r = 0; r < num_seqs; ++r)
+    a.num_groups += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], a.ck) * (int64_t)hkv;
   const int64_t nwg = up::ceil_div(a.num_groups, 8) * 8 * (a.rg > lay.g.rg_a ? a.rg : lay.g.rg_a);
   if (nwg > 0x7fffffff) return up::set_error(UP_ERR_UNSUPPORTED, "grid too large");
   switch (head_dim) {
