@@ -111,6 +111,7 @@ up_status up_score_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int
  *        h*q_head_stride + c].  Only the n_eff tail rows of each request are
  *        read.  q and both strides must be 16-byte / 8-element aligned.
  * k      bf16 [T, hkv, head_dim], same convention; every row is read.
+ *        k_tok_stride <= 2^24 elements (UP_ERR_UNSUPPORTED otherwise).
  * head_dim  64, 128 or 256.    hq % hkv == 0, 1 <= hq <= 1024.
  * n_query   tail queries n, 1..4096.   block  G, a power of two in [16, 256].
  * scale  softmax scale; 0 selects 1/sqrt(head_dim).

@@ -81,6 +81,7 @@ def _score_status(**over):
     (dict(ws_bytes=16), 3, "workspace"),
     (dict(bs=None), 1, "NULL"),
     (dict(ws=300), 1, "256-byte"),
+    (dict(k_tok=(1 << 24) + 8), 2, "k_tok_stride"),
 ])
 def test_score_rejects_bad_arguments(over, status, msg):
     st, err = _score_status(**over)

@@ -22,6 +22,8 @@
 // No floating-point atomics anywhere: results are bitwise reproducible.
 #include <math.h>
 
+#include <type_traits>
+
 #include "up_internal.h"
 
 namespace up {
@@ -139,7 +141,62 @@ struct KTile {
   }
   // Element offset of chunk c of tile row r.
   static __device__ __forceinline__ int offset(int r, int c) { return r * D + ((c ^ (r & SWZ)) << 3); }
+  // Element offset, from the tile's first key, of the 8 elements lane
+  // `lane` moves with load instruction i (the same for every tile).
+  static __device__ __forceinline__ uint32_t lane_offset(int64_t k_tok, int wave, int i, int lane) {
+    const int j = wave * INSTS + i;
+    const int r = j * RPI + lane / CHUNKS;
+    const int c = (lane % CHUNKS) ^ (r & SWZ);
+    return (uint32_t)((int64_t)r * k_tok + c * 8);
+  }
 };
+
+// The chunk's key tiles as a stream into the LDS ring.  Whole tiles use a
+// uniform base address plus fixed per-lane offsets, so a fetch costs no
+// vector address arithmetic; only a chunk's ragged last tile takes the
+// clamped path.
+template <int D, int W>
+struct KStream {
+  using Tile = KTile<D, W>;
+  const uint16_t* kbase;  // key 0 of the request in this KV head
+  int64_t k_tok;
+  int key0, key1, wave, lane;
+  uint32_t off[Tile::INSTS];
+
+  __device__ __forceinline__ void init(const uint16_t* kb, int64_t kt, int k0, int k1, int w, int l) {
+    kbase = kb;
+    k_tok = kt;
+    key0 = k0;
+    key1 = k1;
+    wave = w;
+    lane = l;
+#pragma unroll
+    for (int i = 0; i < Tile::INSTS; ++i) off[i] = Tile::lane_offset(kt, w, i, l);
+  }
+  // Tile t, known to hold KT keys below key1.
+  __device__ __forceinline__ void fetch_full(int t, uint16_t* dst) const {
+    const uint16_t* tb = kbase + (int64_t)(key0 + t * Tile::KT) * k_tok;
+    // Device pass only: the host pass never emits this body, and the
+    // target builtin in a member of a class template shared by two kernels
+    // otherwise invalidates the second kernel's host-side launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int i = 0; i < Tile::INSTS; ++i)
+      __builtin_amdgcn_global_load_lds(tb + off[i], dst + (wave * Tile::INSTS + i) * Tile::RPI * D,
+                                       16, 0, 0);
+#else
+    (void)tb;
+    (void)dst;
+#endif
+  }
+  // Any tile t of the chunk.
+  __device__ __forceinline__ void fetch(int t, uint16_t* dst) const {
+    const int tk = key0 + t * Tile::KT;
+    if (tk + Tile::KT <= key1) fetch_full(t, dst);
+    else Tile::fetch(kbase, k_tok, tk, key1, dst, wave, lane);
+  }
+};
+
 
 // Workgroup barrier that waits only for this wave's LDS operations; the K
 // tile fetches in flight are covered by an explicit wait_vmcnt before it.
@@ -149,15 +206,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Ring start: fetch tiles 0..2 (as many as exist), wait for tiles 0 and 1.
-template <typename Tile>
-__device__ __forceinline__ void ring_prologue(const uint16_t* kbase, int64_t k_tok, int key0,
-                                              int key1, int ntiles, uint16_t (*kl)[Tile::ELEMS],
-                                              int wave, int lane);
-// Ring step: tile it+2 must be resident for the next iteration; tile it+3
-// (fetched this iteration when `more`) may stay in flight.
-template <typename Tile>
-__device__ __forceinline__ void ring_advance(bool more);
-
+template <typename Stream>
+__device__ __forceinline__ void ring_prologue(const Stream& ks, int ntiles,
+                                              uint16_t (*kl)[Stream::Tile::ELEMS]);
 // Wait until at most N of this wave's vector-memory loads (the K tile
 // fetches) are in flight.  Written as an asm statement so the compiler's own
 // wait-count pass keeps it exactly as placed.
@@ -167,26 +218,28 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename Tile>
-__device__ __forceinline__ void ring_prologue(const uint16_t* kbase, int64_t k_tok, int key0,
-                                              int key1, int ntiles, uint16_t (*kl)[Tile::ELEMS],
-                                              int wave, int lane) {
-  Tile::fetch(kbase, k_tok, key0, key1, kl[0], wave, lane);
-  if (ntiles > 1) Tile::fetch(kbase, k_tok, key0 + Tile::KT, key1, kl[1], wave, lane);
+template <typename Stream>
+__device__ __forceinline__ void ring_prologue(const Stream& ks, int ntiles,
+                                              uint16_t (*kl)[Stream::Tile::ELEMS]) {
+  ks.fetch(0, kl[0]);
+  if (ntiles > 1) ks.fetch(1, kl[1]);
   if (ntiles > 2) {
-    Tile::fetch(kbase, k_tok, key0 + 2 * Tile::KT, key1, kl[2], wave, lane);
-    wait_vmcnt<Tile::INSTS>();
+    ks.fetch(2, kl[2]);
+    wait_vmcnt<Stream::Tile::INSTS>();
   } else {
     wait_vmcnt<0>();
   }
   lds_barrier();
 }
 
-template <typename Tile>
-__device__ __forceinline__ void ring_advance(bool more) {
-  if (more) wait_vmcnt<Tile::INSTS>(); else wait_vmcnt<0>();
+// End of one ring iteration: tile it+2 resident in LDS for every wave.
+// FETCHED = tile it+3 was fetched this iteration and may stay in flight.
+template <typename Tile, bool FETCHED>
+__device__ __forceinline__ void ring_step() {
+  if constexpr (FETCHED) wait_vmcnt<Tile::INSTS>(); else wait_vmcnt<0>();
   lds_barrier();
 }
+
 
 // Query fragments of the lane's rows.  Row rho of KV group g is query head
 // g*rgqa + rho/n_eff at tail position rho%n_eff.  The same registers serve as
@@ -348,7 +401,8 @@ up_rowstats_kernel(ScoreArgs a) {
   const int wg_row0 = rgi * (NT * 32 * W);
   if (key0 >= L || wg_row0 >= R) return;  // uniform over the workgroup
   const int key1 = min(L, key0 + a.ck);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row0 = wg_row0 + wave * NT * 32;
   const int qpos0 = L - n_eff;
   const float C = a.c;
@@ -369,29 +423,54 @@ up_rowstats_kernel(ScoreArgs a) {
   // leading tiles that need no mask: every key < key1 and <= every tail row
   const int lim = min(key1, qpos0 + 1);
   const int nfast = lim > key0 ? (lim - key0) / KT : 0;
-  ring_prologue<Tile>(kbase, a.k_tok, key0, key1, ntiles, kl, wave, lane);
+  KStream<D, W> ks;
+  ks.init(kbase, a.k_tok, key0, key1, wave, lane);
+  ring_prologue(ks, ntiles, kl);
 
+  // Mask-free tiles first (software-pipelined when PIPE), then the tiles
+  // that meet the causal diagonal or the chunk's end, in straight order.
+  // The steady-state loop prefetches whole tiles only and waits a fixed
+  // count, so its body stays one basic block the scheduler can interleave;
+  // the last few iterations (no prefetch left or a ragged one) wait for all.
+  const int nfull = (key1 - key0) / KT;
+  const int nmain = max(0, min(nfast, nfull - 3));
   bf16x8_t af[D / 16];
-  f32x16_t acc = {};
-  if constexpr (PIPE) {
-    load_frags<D, W>(kl[0], 0, lane, af);
+  int it = 0;
+  if (nfast > 0) {
+    f32x16_t acc = {};
+    if constexpr (PIPE) {
+      load_frags<D, W>(kl[0], 0, lane, af);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) acc = mfma32(af[s], qf[0][s], acc);
+      for (int s = 0; s < D / 16; ++s) acc = mfma32(af[s], qf[0][s], acc);
+    }
+    // Steady state unrolled over the ring, so every LDS slot address is a
+    // compile-time constant (it starts at 0, a multiple of kRing).
+    auto step = [&](auto u) {
+      constexpr int U = decltype(u)::value;
+      ks.fetch_full(it + U + 3, kl[(U + 3) % kRing]);
+      rowstats_iter<D, NT, W, false, PIPE>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1,
+                                           lane, C, qf, ipos, m_run, l_run, acc, af);
+      ring_step<Tile, true>();
+    };
+    for (; it + kRing <= nmain; it += kRing) {
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+    }
+    for (; it < nfast; ++it) {
+      if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+      rowstats_iter<D, NT, W, false, PIPE>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT,
+                                           key1, lane, C, qf, ipos, m_run, l_run, acc, af);
+      if (it + 3 < ntiles) ring_step<Tile, true>(); else ring_step<Tile, false>();
+    }
   }
-
-  for (int it = 0; it < ntiles; ++it) {
-    const uint16_t* cur = kl[it % kRing];
-    const uint16_t* nxt = kl[(it + 1) % kRing];
-    const int tkey0 = key0 + it * KT;
-    const bool more = it + 3 < ntiles;
-    if (more) Tile::fetch(kbase, a.k_tok, tkey0 + 3 * KT, key1, kl[(it + 3) % kRing], wave, lane);
-    if (it < nfast)
-      rowstats_iter<D, NT, W, false, PIPE>(cur, nxt, tkey0, key1, lane, C, qf, ipos, m_run, l_run,
-                                           acc, af);
-    else
-      rowstats_iter<D, NT, W, true, PIPE>(cur, nxt, tkey0, key1, lane, C, qf, ipos, m_run, l_run,
-                                          acc, af);
-    ring_advance<Tile>(more);
+  for (; it < ntiles; ++it) {
+    if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+    f32x16_t acc = {};
+    rowstats_iter<D, NT, W, true, false>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1,
+                                         lane, C, qf, ipos, m_run, l_run, acc, af);
+    ring_step<Tile, false>();
   }
 
   // Merge the two half-waves (same row, disjoint keys) and write the partial.
@@ -491,7 +570,7 @@ __device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t*
         col += colsum_update<NT>(sacc, t, MASKED, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
       }
       col += __shfl_xor(col, 32);
-      if (lane < 32) colrow[wave][nt * 32 + lane] = col;
+      colrow[wave][nt * 32 + (lane & 31)] = col;  // both halves hold the same sum
       col = 0.f;
     }
     return;
@@ -514,11 +593,27 @@ __device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t*
     col += colsum_update<NT>(acc, t, MASKED, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
     if (t == NT - 1) {
       col += __shfl_xor(col, 32);
-      if (lane < 32) colrow[wave][nt * 32 + lane] = col;
+      colrow[wave][nt * 32 + (lane & 31)] = col;  // both halves hold the same sum
       col = 0.f;
     }
     acc = nacc;
     if (PIPE) interleave_hint<D>();
+  }
+}
+
+// After the ring barrier of a tile: one thread per key adds the waves'
+// column sums in wave order and writes the key's partial.
+template <int W, int KT>
+__device__ __forceinline__ void colsum_flush(const float (*colrow)[64], int tid, int tkey0, int key1,
+                                             float* colout) {
+  if (tid < KT) {
+    const int key = tkey0 + tid;
+    if (key < key1) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) sum += colrow[w][tid];
+      colout[key] = sum;
+    }
   }
 }
 
@@ -541,7 +636,8 @@ up_colsum_kernel(ScoreArgs a) {
   const int wg_row0 = rgi * (NT * 32 * W);
   if (key0 >= L || wg_row0 >= R) return;
   const int key1 = min(L, key0 + a.ck);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row0 = wg_row0 + wave * NT * 32;
   const int qpos0 = L - n_eff;
   const float C = a.c;
@@ -571,39 +667,55 @@ up_colsum_kernel(ScoreArgs a) {
   const int ntiles = (key1 - key0 + KT - 1) / KT;
   const int lim = min(key1, qpos0 + 1);
   const int nfast = lim > key0 ? (lim - key0) / KT : 0;
-  ring_prologue<Tile>(kbase, a.k_tok, key0, key1, ntiles, kl, wave, lane);
+  KStream<D, W> ks;
+  ks.init(kbase, a.k_tok, key0, key1, wave, lane);
+  ring_prologue(ks, ntiles, kl);
 
+  // Loop structure as in pass A: steady state with whole-tile prefetch and
+  // a fixed wait, then the last mask-free tiles, then the masked tiles.
+  const int nfull = (key1 - key0) / KT;
+  const int nmain = max(0, min(nfast, nfull - 3));
   bf16x8_t kf[D / 16];
-  f32x16_t acc = {};
-  if constexpr (PIPE) {
-    load_frags<D, W>(kl[0], 0, lane, kf);
+  int it = 0;
+  if (nfast > 0) {
+    f32x16_t acc = {};
+    if constexpr (PIPE) {
+      load_frags<D, W>(kl[0], 0, lane, kf);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) acc = mfma32(qf[0][s], kf[s], acc);
-  }
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int cb = it & 1;
-    const uint16_t* cur = kl[it % kRing];
-    const uint16_t* nxt = kl[(it + 1) % kRing];
-    const int tkey0 = key0 + it * KT;
-    const bool more = it + 3 < ntiles;
-    if (more) Tile::fetch(kbase, a.k_tok, tkey0 + 3 * KT, key1, kl[(it + 3) % kRing], wave, lane);
-    if (it < nfast)
-      colsum_iter<D, NT, W, false, PIPE>(cur, nxt, tkey0, key1, lane, wave, row0, R, n_eff, qpos0, C,
-                                         qf, bv, colbuf[cb], acc, kf);
-    else
-      colsum_iter<D, NT, W, true, PIPE>(cur, nxt, tkey0, key1, lane, wave, row0, R, n_eff, qpos0, C,
-                                        qf, bv, colbuf[cb], acc, kf);
-    ring_advance<Tile>(more);
-    if (tid < KT) {
-      const int key = tkey0 + tid;
-      if (key < key1) {
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) sum += colbuf[cb][w][tid];
-        colout[key] = sum;
-      }
+      for (int s = 0; s < D / 16; ++s) acc = mfma32(qf[0][s], kf[s], acc);
     }
+    auto step = [&](auto u) {
+      constexpr int U = decltype(u)::value;
+      ks.fetch_full(it + U + 3, kl[(U + 3) % kRing]);
+      colsum_iter<D, NT, W, false, PIPE>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1,
+                                         lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
+                                         colbuf[U & 1], acc, kf);
+      ring_step<Tile, true>();
+      colsum_flush<W, KT>(colbuf[U & 1], tid, key0 + (it + U) * KT, key1, colout);
+    };
+    for (; it + kRing <= nmain; it += kRing) {
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+    }
+    for (; it < nfast; ++it) {
+      if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+      colsum_iter<D, NT, W, false, PIPE>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1,
+                                         lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
+                                         colbuf[it & 1], acc, kf);
+      if (it + 3 < ntiles) ring_step<Tile, true>(); else ring_step<Tile, false>();
+      colsum_flush<W, KT>(colbuf[it & 1], tid, key0 + it * KT, key1, colout);
+    }
+  }
+  for (; it < ntiles; ++it) {
+    if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+    f32x16_t acc = {};
+    colsum_iter<D, NT, W, true, false>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1,
+                                       lane, wave, row0, R, n_eff, qpos0, C, qf, bv, colbuf[it & 1],
+                                       acc, kf);
+    ring_step<Tile, false>();
+    colsum_flush<W, KT>(colbuf[it & 1], tid, key0 + it * KT, key1, colout);
   }
 }
 
@@ -646,11 +758,23 @@ __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
 // Compile-time tiling per head_dim and pass: NT 32-row tiles per wave, W
 // waves per workgroup, PIPE = software-pipelined MFMA/VALU interleave.  Pass A
 // writes per-row partials, so the two passes may group rows differently.
+#ifndef UP_TILE_A64
+#define UP_TILE_A64 2, 4, true
+#endif
+#ifndef UP_TILE_B64
+#define UP_TILE_B64 2, 8, true
+#endif
 #ifndef UP_TILE_A128
 #define UP_TILE_A128 2, 4, true
 #endif
 #ifndef UP_TILE_B128
-#define UP_TILE_B128 2, 8, false
+#define UP_TILE_B128 2, 8, true
+#endif
+#ifndef UP_TILE_A256
+#define UP_TILE_A256 1, 4, true
+#endif
+#ifndef UP_TILE_B256
+#define UP_TILE_B256 1, 4, false
 #endif
 template <int NT_, int W_, bool PIPE_>
 struct TileCfg {
@@ -659,9 +783,9 @@ struct TileCfg {
   static constexpr int ROWS = NT * 32 * W;
 };
 template <int D> struct Tiling;
-template <> struct Tiling<64> { using A = TileCfg<2, 4, true>; using B = TileCfg<2, 4, false>; };
+template <> struct Tiling<64> { using A = TileCfg<UP_TILE_A64>; using B = TileCfg<UP_TILE_B64>; };
 template <> struct Tiling<128> { using A = TileCfg<UP_TILE_A128>; using B = TileCfg<UP_TILE_B128>; };
-template <> struct Tiling<256> { using A = TileCfg<1, 4, true>; using B = TileCfg<1, 4, false>; };
+template <> struct Tiling<256> { using A = TileCfg<UP_TILE_A256>; using B = TileCfg<UP_TILE_B256>; };
 
 int rows_per_wg_for(int d, bool pass_b) {
   switch (d) {
@@ -814,6 +938,9 @@ up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_
                          "q/k must be 16-byte aligned with strides that are multiples of 8 elements");
   if (q_tok_stride < 0 || q_head_stride < 0 || k_tok_stride < 0 || k_head_stride < 0)
     return up::set_error(UP_ERR_INVALID, "negative stride");
+  if (k_tok_stride > (int64_t(1) << 24))
+    return up::set_error(UP_ERR_UNSUPPORTED, "k_tok_stride %lld > 2^24 elements",
+                         (long long)k_tok_stride);
   if ((uintptr_t)workspace & 255) return up::set_error(UP_ERR_INVALID, "workspace not 256-byte aligned");
   if (workspace_bytes < lay.bytes)
     return up::set_error(UP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes,
