@@ -72,8 +72,9 @@ def load_traffic(kernel: str, src: str, launches_per_call: int = 1):
 
 
 COPY_BYTES = 1 << 30
-TRAFFIC_KERNELS = {"up_compact_kernel": "up_compact.hip", "up_rowstats_kernel": "up_score.hip",
-                   "up_colsum_kernel": "up_score.hip", "up_select_kernel": "up_select.hip"}
+TRAFFIC_KERNELS = {"up_compact_copy_kernel": "up_compact.hip", "up_compact_scan_kernel": "up_compact.hip",
+                   "up_rowstats_kernel": "up_score.hip", "up_colsum_kernel": "up_score.hip",
+                   "up_select_kernel": "up_select.hip"}
 
 
 def write_traffic(fetch_csv: str, write_csv: str) -> None:
@@ -223,11 +224,17 @@ def main():
     score_tflops_alg = flops_alg / t_score / 1e12
 
     if t_compact >= t_score:
-        traffic = load_traffic("up_compact_kernel", "up_compact.hip")
-        roofline = {"kernel": "up_compact_kernel", "bound": "hbm", "achieved": round(compact_gbs, 1),
+        # The copy kernel moves every byte; the events bracket the whole
+        # up_compact call (its small scan launch included), so `achieved`
+        # slightly understates the copy kernel's own rate.
+        tc = load_traffic("up_compact_copy_kernel", "up_compact.hip")
+        ts = load_traffic("up_compact_scan_kernel", "up_compact.hip")
+        traffic = tc + ts if tc is not None and ts is not None else None
+        roofline = {"kernel": "up_compact_copy_kernel", "bound": "hbm", "achieved": round(compact_gbs, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
                     "traffic": traffic,
-                    "algorithmic_bytes_per_launch": int(compact_bytes)}
+                    "algorithmic_bytes_per_launch": int(compact_bytes),
+                    "duration": "HIP events around up_compact (scan + copy launches)"}
     else:
         roofline = {"kernel": "up_score (rowstats+combine+colsum+blockmean)", "bound": "mfma",
                     "achieved": round(score_tflops_exec, 1), "peak": PEAK_BF16_TFLOPS,

@@ -161,7 +161,8 @@ up_status up_select_topp(int num_seqs, const int32_t* cu_seqlens_h, const int32_
 /* Step 5: compaction (§二 step 3, §三 metadata update)                       */
 /* ------------------------------------------------------------------------ */
 
-/* Workspace bytes up_compact needs for this batch (tile status words). */
+/* Workspace bytes up_compact needs for this batch (control and status words,
+ * one 16-byte copy descriptor per block). */
 up_status up_compact_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int block,
                                     size_t* bytes);
 
@@ -190,11 +191,12 @@ up_status up_compact_workspace_init(void* workspace, size_t workspace_bytes, hip
  * workspace        >= up_compact_workspace_size bytes, 256-byte aligned,
  *                  prepared by up_compact_workspace_init (and then only
  *                  used by up_compact calls, one at a time).
- * One kernel launch: a single-pass decoupled look-back scan (Merrill &
- * Garland 2016) over tiles of blocks gives each tile its output offset
- * (tiles are claimed in order from an atomic counter, so every look-back
- * ends) and the tile copies its kept rows; the last tile to finish restores
- * the workspace for the next call.
+ * Two kernel launches: a single-pass decoupled look-back scan (Merrill &
+ * Garland 2016) over tiles of 1024 blocks writes each block's output row
+ * and cu_seqlens_out (tiles are claimed in order from an atomic counter, so
+ * every look-back ends; the last tile to finish restores the workspace's
+ * control and status words for the next call), then a copy kernel moves
+ * each kept block in 64 KiB pieces.
  */
 up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                      const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,

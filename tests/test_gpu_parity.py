@@ -195,7 +195,10 @@ def test_compact_isolated(dtype, dim, strided):
         assert (pout[n:] == -1).all() and (out[n:] == 0).all()   # nothing past the kept rows
         _, _, cu_ref = O.compact(mask_np, np.zeros((T, 1)), np.zeros(T), cu.numpy(), G)
         assert list(cu_out.cpu().numpy()) == list(cu_ref)
-        assert not ws.view(torch.int32)[:2].any() and not ws[256:].any()   # left clean
+        # left clean: ticket and done counter, and the scan tiles' status words
+        # (one per 1024 blocks, after the 256-byte control block)
+        tiles = -(-batch.num_blocks // 1024)
+        assert not ws.view(torch.int32)[:2].any() and not ws[256:256 + 8 * tiles].any()
 
 
 def test_compact_all_empty_and_no_positions():

@@ -6,28 +6,36 @@
 // with updated per-request lengths, and each drop appends (layer id, kept
 // tokens) to the request's drop-history ledger.
 //
-// up_compact is one kernel: a single-pass decoupled look-back scan (Merrill & Garland, "Single-pass Parallel Prefix
-// Scan with Decoupled Look-back", 2016) over tiles of whole blocks.  Each
-// workgroup claims the next tile from an atomic ticket (so every tile it may
-// wait on has already started), publishes its kept-token count, walks back
-// over its predecessors' published counts to get its output offset, publishes
-// the inclusive count, and copies its kept blocks.  Because the mask is per
-// block, a kept block is a run of G consecutive rows, copied as one flat
-// byte range with wide vector loads and stores; dropped rows are never read.
-// Every status word carries its state and its count in one 64-bit atomic and
-// no tile reads data another tile wrote, so relaxed device-scope atomics are
-// enough: release/acquire at device scope would write back / invalidate the
-// XCD's L2 on every publish and poll, which stalls the copy.
-// The last workgroup to finish (a done counter) clears the tile status words
-// and both counters, so the next call starts from a clean workspace without
-// a separate clearing launch; up_compact_workspace_init prepares a new one.
+// up_compact is two kernels.
+//   up_compact_scan_kernel   single-pass decoupled look-back scan (Merrill &
+//     Garland, "Single-pass Parallel Prefix Scan with Decoupled Look-back",
+//     2016) over tiles of 1024 blocks: each workgroup claims the next tile
+//     from an atomic ticket (so every tile it may wait on has already
+//     started), publishes its kept-token count, walks back over its
+//     predecessors' published counts to get its output offset, publishes the
+//     inclusive count, and writes one copy descriptor per block (destination
+//     row, source row, rows) plus cu_seqlens_out.  Every status word carries
+//     its state and its count in one 64-bit atomic and no tile reads data
+//     another tile wrote, so relaxed device-scope atomics are enough:
+//     release/acquire at device scope would write back / invalidate the XCD's
+//     L2 on every publish and poll.  The last workgroup to finish (a done
+//     counter) clears the status words and both counters, so the next call
+//     starts from a clean workspace without a separate clearing launch.
+//   up_compact_copy_kernel   one workgroup per (block, 64 KiB piece): a kept
+//     block is a run of G consecutive rows, copied as one flat byte range with
+//     16-byte non-temporal loads and stores; dropped rows are never read.
+// Splitting the gather from the scan lets the copy use small, uniform work
+// items (the shape a plain device copy runs fastest with) instead of one
+// workgroup per scan tile.
 #include "up_internal.h"
 
 namespace up {
 namespace {
 
 constexpr int kCompactThreads = 256;
-constexpr int kMaxTileBlocks = 64;
+constexpr int kScanPerThread = 4;
+constexpr int kScanTileBlocks = kCompactThreads * kScanPerThread;  // blocks per scan tile
+constexpr int64_t kPieceBytes = 64 << 10;                          // bytes per copy work item
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
@@ -35,6 +43,14 @@ constexpr int kSpinLimit = 1 << 24;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Copy descriptor of one block: dst < 0 marks a dropped block (or one that
+// would not fit the output capacity).
+struct BlockCopy {
+  int64_t dst;  // first output row
+  int32_t src;  // first input row
+  int32_t rows;
+};
 
 struct CompactArgs {
   const int32_t* cu_seqlens;
@@ -45,10 +61,13 @@ struct CompactArgs {
   char* hidden_out;
   int32_t* positions_out;
   int32_t* cu_out;
-  uint64_t* flags;    // [num_tiles] tile status words
+  uint64_t* flags;    // [num_tiles] scan tile status words
   uint32_t* ctl;      // [0] tile ticket, [1] done counter, [2] sticky look-back timeout flag
+  BlockCopy* desc;    // [num_blocks]
   int64_t row_bytes, row_stride, capacity, num_blocks, num_tiles;
-  int num_seqs, block, tile_blocks;
+  int64_t pieces;     // copy work items per block
+  int64_t piece_rows; // rows per work item when rows are strided
+  int num_seqs, block;
 };
 
 // Zero a whole compaction workspace (control words and tile status words).
@@ -57,55 +76,21 @@ __global__ void up_compact_init_kernel(uint32_t* ws, int64_t nwords) {
   if (i < nwords) ws[i] = 0;
 }
 
-template <int VW> struct Vec;
-template <> struct Vec<16> { typedef u32x4_t T; };
-template <> struct Vec<8> { typedef u32x2_t T; };
-template <> struct Vec<4> { typedef uint32_t T; };
-template <> struct Vec<1> { typedef uint8_t T; };
-
-// Copy nbytes (a multiple of VW) from src to dst, whole workgroup.
-template <int VW>
-__device__ __forceinline__ void copy_flat(char* __restrict__ dst, const char* __restrict__ src,
-                                          int64_t nbytes) {
-  typedef typename Vec<VW>::T V;
-  constexpr int U = 4;
-  const V* s = reinterpret_cast<const V*>(src);
-  V* d = reinterpret_cast<V*>(dst);
-  const int64_t n = nbytes / VW;
-  int64_t i = threadIdx.x;
-  for (; i + (U - 1) * kCompactThreads < n; i += U * kCompactThreads) {
-    V r[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = __builtin_nontemporal_load(s + i + u * kCompactThreads);
-#pragma unroll
-    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(r[u], d + i + u * kCompactThreads);
+// Request owning block b: the last r with cu_blocks[r] <= b.
+__device__ __forceinline__ int block_request(const int32_t* cu_blocks, int num_seqs, int64_t b) {
+  int lo = 0, hi = num_seqs;  // cu_blocks[lo] <= b < cu_blocks[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu_blocks[mid] <= b) lo = mid; else hi = mid;
   }
-  for (; i < n; i += kCompactThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
+  return lo;
 }
 
-// Copy `rows` rows of row_bytes from a strided source to a packed destination
-// (one wave per row; not the hot path: the packed case goes through copy_flat).
-template <int VW>
-__device__ __forceinline__ void copy_rows(char* __restrict__ dst, const char* __restrict__ src,
-                                          int rows, int64_t row_bytes, int64_t row_stride) {
-  typedef typename Vec<VW>::T V;
-  const int64_t vpr = row_bytes / VW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = wave; r < rows; r += kCompactThreads / 64) {
-    const V* s = reinterpret_cast<const V*>(src + (int64_t)r * row_stride);
-    V* d = reinterpret_cast<V*>(dst + (int64_t)r * row_bytes);
-    for (int64_t c = lane; c < vpr; c += 64) __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
-  }
-}
-
-template <int VW>
-__global__ void __launch_bounds__(kCompactThreads) up_compact_kernel(CompactArgs a) {
+__global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(CompactArgs a) {
   __shared__ int64_t s_tile;
   __shared__ int64_t s_excl;
+  __shared__ int64_t s_wave[kCompactThreads / 64];
   __shared__ int s_last;
-  __shared__ int s_src[kMaxTileBlocks];     // first source token of each block
-  __shared__ int s_size[kMaxTileBlocks];    // rows of each block if kept, else 0
-  __shared__ int64_t s_dst[kMaxTileBlocks]; // in-tile exclusive prefix of kept rows
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_tile = (int64_t)atomicAdd(&a.ctl[0], 1u);
@@ -120,38 +105,45 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_kernel(CompactArgs
   }
 
   if (t < a.num_tiles) {
-    const int64_t b0 = t * a.tile_blocks;
-    const int nblk = (int)min((int64_t)a.tile_blocks, a.num_blocks - b0);
+    // This thread's blocks: kScanPerThread consecutive ones.
+    const int64_t b0 = t * kScanTileBlocks + (int64_t)tid * kScanPerThread;
+    int req[kScanPerThread], rows[kScanPerThread];
+    int64_t kept[kScanPerThread];
+    int64_t mine = 0;
+    int r = b0 < a.num_blocks ? block_request(a.cu_blocks, a.num_seqs, b0) : 0;
+#pragma unroll
+    for (int i = 0; i < kScanPerThread; ++i) {
+      const int64_t b = b0 + i;
+      req[i] = -1;
+      rows[i] = 0;
+      kept[i] = 0;
+      if (b < a.num_blocks) {
+        while (a.cu_blocks[r + 1] <= b) ++r;  // skip to the owning request
+        const int L = a.cu_seqlens[r + 1] - a.cu_seqlens[r];
+        const int lb = (int)(b - a.cu_blocks[r]);
+        req[i] = r;
+        rows[i] = min(lb * a.block + a.block, L) - lb * a.block;
+        kept[i] = a.mask[b] ? rows[i] : 0;
+        mine += kept[i];
+      }
+    }
+    // Exclusive scan of the threads' kept rows: waves, then across waves.
+    int64_t incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int64_t wbase = 0, agg = 0;
+#pragma unroll
+    for (int w = 0; w < kCompactThreads / 64; ++w) {
+      if (w < wave) wbase += s_wave[w];
+      agg += s_wave[w];
+    }
 
     if (wave == 0) {
-      int64_t ksize = 0;
-      int req = 0, lb = 0;
-      if (lane < nblk) {
-        const int64_t b = b0 + lane;
-        int lo = 0, hi = a.num_seqs;  // cu_blocks[lo] <= b < cu_blocks[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
-        }
-        req = lo;
-        const int s0 = a.cu_seqlens[req];
-        const int L = a.cu_seqlens[req + 1] - s0;
-        lb = (int)(b - a.cu_blocks[req]);
-        const int size = min(lb * a.block + a.block, L) - lb * a.block;
-        ksize = a.mask[b] ? size : 0;
-        s_src[lane] = s0 + lb * a.block;
-        s_size[lane] = (int)ksize;
-      }
-      // inclusive scan of kept rows across the tile's blocks
-      int64_t incl = ksize;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int64_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const int64_t agg = __shfl(incl, 63);
-      if (lane < nblk) s_dst[lane] = incl - ksize;
-
       // Publish this tile's count, then look back a window of 64
       // predecessors per round trip: lane i reads tile (hi - i); the nearest
       // tile that already has an inclusive prefix ends the walk.
@@ -187,38 +179,29 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_kernel(CompactArgs
                              __HIP_MEMORY_SCOPE_AGENT);
       }
       if (lane == 0) s_excl = excl;
-
-      // Requests whose last block is in this tile (and empty requests right
-      // after them) end at this block's inclusive count.
-      if (lane < nblk) {
-        const int nb_r = a.cu_blocks[req + 1] - a.cu_blocks[req];
-        if (lb == nb_r - 1) {
-          const int32_t end = (int32_t)(excl + incl);
-          a.cu_out[req + 1] = end;
-          const int32_t bend = a.cu_blocks[req + 1];
-          for (int r2 = req + 1; r2 < a.num_seqs && a.cu_blocks[r2 + 1] == bend; ++r2)
-            a.cu_out[r2 + 1] = end;
-        }
-      }
     }
     __syncthreads();
 
-    const int64_t excl = s_excl;
-    for (int i = 0; i < nblk; ++i) {
-      const int rows = s_size[i];
-      if (rows == 0) continue;
-      const int64_t dst_row = excl + s_dst[i];
-      if (dst_row + rows > a.capacity) continue;  // never write past the output
-      const int64_t src_row = s_src[i];
-      if (a.row_stride == a.row_bytes)
-        copy_flat<VW>(a.hidden_out + dst_row * a.row_bytes, a.hidden + src_row * a.row_bytes,
-                      (int64_t)rows * a.row_bytes);
-      else
-        copy_rows<VW>(a.hidden_out + dst_row * a.row_bytes, a.hidden + src_row * a.row_stride, rows,
-                      a.row_bytes, a.row_stride);
-      if (a.positions)
-        for (int i2 = tid; i2 < rows; i2 += kCompactThreads)
-          a.positions_out[dst_row + i2] = a.positions[src_row + i2];
+    // Descriptors and request ends.
+    int64_t pos = s_excl + wbase + incl - mine;  // this thread's first output row
+#pragma unroll
+    for (int i = 0; i < kScanPerThread; ++i) {
+      const int64_t b = b0 + i;
+      if (req[i] < 0) continue;
+      const int rq = req[i];
+      BlockCopy d;
+      d.dst = (kept[i] > 0 && pos + kept[i] <= a.capacity) ? pos : -1;  // never past the output
+      d.src = a.cu_seqlens[rq] + (int)(b - a.cu_blocks[rq]) * a.block;
+      d.rows = rows[i];
+      a.desc[b] = d;
+      pos += kept[i];
+      // A request whose last block this is (and empty requests right after
+      // it) ends at this block's inclusive count.
+      if (b == a.cu_blocks[rq + 1] - 1) {
+        a.cu_out[rq + 1] = (int32_t)pos;
+        for (int r2 = rq + 1; r2 < a.num_seqs && a.cu_blocks[r2 + 1] == a.cu_blocks[rq + 1]; ++r2)
+          a.cu_out[r2 + 1] = (int32_t)pos;
+      }
     }
   }
 
@@ -238,6 +221,76 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_kernel(CompactArgs
       a.ctl[0] = 0;
       a.ctl[1] = 0;
     }
+  }
+}
+
+template <int VW> struct Vec;
+template <> struct Vec<16> { typedef u32x4_t T; };
+template <> struct Vec<8> { typedef u32x2_t T; };
+template <> struct Vec<4> { typedef uint32_t T; };
+template <> struct Vec<1> { typedef uint8_t T; };
+
+// Copy nbytes (a multiple of VW) from src to dst, whole workgroup, four
+// vectors in flight per lane.
+template <int VW>
+__device__ __forceinline__ void copy_flat(char* __restrict__ dst, const char* __restrict__ src,
+                                          int64_t nbytes) {
+  typedef typename Vec<VW>::T V;
+  constexpr int U = 4;
+  const V* s = reinterpret_cast<const V*>(src);
+  V* d = reinterpret_cast<V*>(dst);
+  const int64_t n = nbytes / VW;
+  int64_t i = threadIdx.x;
+  for (; i + (U - 1) * kCompactThreads < n; i += U * kCompactThreads) {
+    V r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = __builtin_nontemporal_load(s + i + u * kCompactThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(r[u], d + i + u * kCompactThreads);
+  }
+  for (; i < n; i += kCompactThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
+}
+
+// Copy `rows` rows of row_bytes from a strided source to a packed
+// destination, one wave per row.
+template <int VW>
+__device__ __forceinline__ void copy_rows(char* __restrict__ dst, const char* __restrict__ src,
+                                          int rows, int64_t row_bytes, int64_t row_stride) {
+  typedef typename Vec<VW>::T V;
+  const int64_t vpr = row_bytes / VW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = wave; r < rows; r += kCompactThreads / 64) {
+    const V* s = reinterpret_cast<const V*>(src + (int64_t)r * row_stride);
+    V* d = reinterpret_cast<V*>(dst + (int64_t)r * row_bytes);
+    for (int64_t c = lane; c < vpr; c += 64) __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
+  }
+}
+
+// Work item w = (block w / pieces, piece w % pieces); a grid-stride loop
+// covers grids capped below the launch limit.
+template <int VW>
+__global__ void __launch_bounds__(kCompactThreads) up_compact_copy_kernel(CompactArgs a) {
+  const int64_t items = a.num_blocks * a.pieces;
+  for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+    const int64_t b = w / a.pieces, piece = w - b * a.pieces;
+    const BlockCopy d = a.desc[b];
+    if (d.dst < 0) continue;  // uniform over the workgroup
+    if (a.row_stride == a.row_bytes) {
+      const int64_t bytes = (int64_t)d.rows * a.row_bytes;
+      const int64_t p0 = piece * kPieceBytes;
+      if (p0 < bytes)
+        copy_flat<VW>(a.hidden_out + d.dst * a.row_bytes + p0, a.hidden + d.src * a.row_bytes + p0,
+                      min(kPieceBytes, bytes - p0));
+    } else {
+      const int64_t r0 = piece * a.piece_rows;
+      if (r0 < d.rows)
+        copy_rows<VW>(a.hidden_out + (d.dst + r0) * a.row_bytes,
+                      a.hidden + (d.src + r0) * a.row_stride, (int)min(a.piece_rows, d.rows - r0),
+                      a.row_bytes, a.row_stride);
+    }
+    if (a.positions && piece == 0)
+      for (int i = threadIdx.x; i < d.rows; i += kCompactThreads)
+        a.positions_out[d.dst + i] = a.positions[d.src + i];
   }
 }
 
@@ -280,18 +333,29 @@ __global__ void up_history_append_kernel(int32_t* led, int num_seqs, int capacit
 }  // namespace
 
 int compact_tile_blocks(int block) {
-  int tb = 64 / block;
-  return tb < 1 ? 1 : tb;
+  (void)block;
+  return kScanTileBlocks;
 }
 
 }  // namespace up
 
 namespace {
 
-int64_t compact_tiles(int num_seqs, const int32_t* cu_h, int block) {
-  int64_t N = 0;
-  for (int r = 0; r < num_seqs; ++r) N += up::ceil_div(cu_h[r + 1] - cu_h[r], block);
-  return up::ceil_div(N, up::compact_tile_blocks(block));
+// Workspace: 256 bytes of control words, the scan tiles' status words, then
+// one copy descriptor per block.
+struct CompactLayout {
+  int64_t blocks, tiles;
+  size_t off_flags, off_desc, bytes;
+};
+
+CompactLayout compact_layout(int num_seqs, const int32_t* cu_h, int block) {
+  CompactLayout l{};
+  for (int r = 0; r < num_seqs; ++r) l.blocks += up::ceil_div(cu_h[r + 1] - cu_h[r], block);
+  l.tiles = up::ceil_div(l.blocks, up::compact_tile_blocks(block));
+  l.off_flags = 256;
+  l.off_desc = up::align_up(l.off_flags + (size_t)l.tiles * sizeof(uint64_t), 256);
+  l.bytes = up::align_up(l.off_desc + (size_t)l.blocks * sizeof(up::BlockCopy), 256);
+  return l;
 }
 
 }  // namespace
@@ -307,8 +371,7 @@ up_status up_compact_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, i
   int mx;
   up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &mx);
   if (st != UP_OK) return st;
-  const int64_t tiles = compact_tiles(num_seqs, cu_seqlens_h, block);
-  *bytes = up::align_up(256 + (size_t)tiles * sizeof(uint64_t), 256);
+  *bytes = compact_layout(num_seqs, cu_seqlens_h, block).bytes;
   return UP_OK;
 }
 
@@ -358,6 +421,7 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   st = up::check_device();
   if (st != UP_OK) return st;
 
+  const CompactLayout lay = compact_layout(num_seqs, cu_seqlens_h, block);
   up::CompactArgs a{};
   a.cu_seqlens = cu_seqlens_d;
   a.cu_blocks = cu_blocks_d;
@@ -368,30 +432,42 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   a.positions_out = positions_out;
   a.cu_out = cu_seqlens_out;
   a.ctl = static_cast<uint32_t*>(workspace);
-  a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + 256);
+  a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + lay.off_flags);
+  a.desc = reinterpret_cast<up::BlockCopy*>(static_cast<char*>(workspace) + lay.off_desc);
   a.row_bytes = row_bytes;
   a.row_stride = row_stride_bytes;
   a.capacity = out_capacity_rows;
   a.num_seqs = num_seqs;
   a.block = block;
-  a.tile_blocks = up::compact_tile_blocks(block);
-  int64_t N = 0;
-  for (int r = 0; r < num_seqs; ++r) N += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], block);
-  a.num_blocks = N;
-  a.num_tiles = up::ceil_div(N, a.tile_blocks);
+  a.num_blocks = lay.blocks;
+  a.num_tiles = lay.tiles;
+  if (row_stride_bytes == row_bytes) {
+    a.pieces = up::ceil_div((int64_t)block * row_bytes, up::kPieceBytes);
+    a.piece_rows = block;
+  } else {
+    a.piece_rows = row_bytes >= up::kPieceBytes ? 1 : up::kPieceBytes / row_bytes;
+    if (a.piece_rows > block) a.piece_rows = block;
+    a.pieces = up::ceil_div(block, a.piece_rows);
+  }
 
+  hipLaunchKernelGGL(up::up_compact_scan_kernel, dim3((unsigned)(a.num_tiles > 0 ? a.num_tiles : 1)),
+                     dim3(up::kCompactThreads), 0, stream, a);
+  st = up::check_launch("up_compact_scan_kernel");
+  if (st != UP_OK || a.num_blocks == 0) return st;
+
+  const int64_t items = a.num_blocks * a.pieces;
+  const dim3 grid((unsigned)(items < (int64_t)1 << 30 ? items : (int64_t)1 << 30));
   const uintptr_t al = (uintptr_t)hidden | (uintptr_t)hidden_out | (uintptr_t)row_bytes |
                        (uintptr_t)row_stride_bytes;
-  const dim3 grid((unsigned)(a.num_tiles > 0 ? a.num_tiles : 1));
   if ((al & 15) == 0)
-    hipLaunchKernelGGL(up::up_compact_kernel<16>, grid, dim3(up::kCompactThreads), 0, stream, a);
+    hipLaunchKernelGGL(up::up_compact_copy_kernel<16>, grid, dim3(up::kCompactThreads), 0, stream, a);
   else if ((al & 7) == 0)
-    hipLaunchKernelGGL(up::up_compact_kernel<8>, grid, dim3(up::kCompactThreads), 0, stream, a);
+    hipLaunchKernelGGL(up::up_compact_copy_kernel<8>, grid, dim3(up::kCompactThreads), 0, stream, a);
   else if ((al & 3) == 0)
-    hipLaunchKernelGGL(up::up_compact_kernel<4>, grid, dim3(up::kCompactThreads), 0, stream, a);
+    hipLaunchKernelGGL(up::up_compact_copy_kernel<4>, grid, dim3(up::kCompactThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(up::up_compact_kernel<1>, grid, dim3(up::kCompactThreads), 0, stream, a);
-  return up::check_launch("up_compact_kernel");
+    hipLaunchKernelGGL(up::up_compact_copy_kernel<1>, grid, dim3(up::kCompactThreads), 0, stream, a);
+  return up::check_launch("up_compact_copy_kernel");
 }
 
 size_t up_history_bytes(int num_seqs, int capacity) {
