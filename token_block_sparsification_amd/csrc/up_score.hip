@@ -51,7 +51,7 @@ struct ScoreArgs {
   int64_t num_groups;  // real (request, KV head, key chunk) groups
   float c;  // scale * log2(e)
   float2* partial;  // [B][hq][n_query][max_chunks] (raw max, sum of exp2)
-  float* bias;      // [B][hq][n_query]
+  float* bias;      // [B][hkv][rgqa * n_query], row order of the KV group
   float* colpart;   // [hkv * rg][T]
   int64_t T;
   float* token_scores;
@@ -287,6 +287,14 @@ __device__ __forceinline__ float tree_sum16(const float (&e)[16]) {
   return (a0 + a1) + (a2 + a3);
 }
 
+// Sum of a value over the two half-waves (lanes l and l ^ 32), in every
+// lane, with the cross-half permute on the VALU (no LDS round trip).
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Interleave hint for one group: one MFMA then a few VALU ops, D/16 times.
 template <int D>
 __device__ __forceinline__ void interleave_hint() {
@@ -514,7 +522,12 @@ __global__ void __launch_bounds__(256) up_rowstats_combine_kernel(ScoreArgs a) {
   for (int c = lane; c < nch; c += 64) l += pp[c].y * fast_exp2(fmaf(pp[c].x, a.c, -mc));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-  if (lane == 0) a.bias[idx] = mc + log2f(l);
+  // Stored in row order of the KV group: row rho = (h % rgqa) * n_eff + ti.
+  if (lane == 0) {
+    const int h = (int)(idx / a.n_query % a.hq);
+    const int g = h / a.rgqa, rho = (h - g * a.rgqa) * n_eff + ti;
+    a.bias[((int64_t)req * a.hkv + g) * a.rgqa * a.n_query + rho] = mc + log2f(l);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -569,7 +582,7 @@ __device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t*
         for (int s = 0; s < D / 16; ++s) sacc = mfma32(qf[t][s], kf[s], sacc);
         col += colsum_update<NT>(sacc, t, MASKED, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
       }
-      col += __shfl_xor(col, 32);
+      col = sum_halves(col);
       colrow[wave][nt * 32 + (lane & 31)] = col;  // both halves hold the same sum
       col = 0.f;
     }
@@ -592,7 +605,7 @@ __device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t*
     const int key = tkey0 + nt * 32 + (lane & 31);
     col += colsum_update<NT>(acc, t, MASKED, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
     if (t == NT - 1) {
-      col += __shfl_xor(col, 32);
+      col = sum_halves(col);
       colrow[wave][nt * 32 + (lane & 31)] = col;  // both halves hold the same sum
       col = 0.f;
     }
@@ -601,20 +614,21 @@ __device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t*
   }
 }
 
-// After the ring barrier of a tile: one thread per key adds the waves'
-// column sums in wave order and writes the key's partial.
-template <int W, int KT>
-__device__ __forceinline__ void colsum_flush(const float (*colrow)[64], int tid, int tkey0, int key1,
-                                             float* colout) {
-  if (tid < KT) {
-    const int key = tkey0 + tid;
-    if (key < key1) {
-      float sum = 0.f;
+// Column partials of a finished tile (its waves' sums in colrow, complete
+// after the tile's ring barrier): every wave adds the W wave sums, in wave
+// order, for its KT/W keys and writes them.  All 64 lanes run it; lanes that
+// share a key store the same value, so no lane mask splits the caller's
+// block.  FULL: every key of the tile is below key1.
+template <int W, int KT, bool FULL>
+__device__ __forceinline__ void colsum_flush(const float (*colrow)[64], int wave, int lane, int tkey0,
+                                             int key1, float* colout) {
+  constexpr int KPW = KT / W;
+  static_assert(KT % W == 0, "keys per wave");
+  const int k = wave * KPW + (lane % KPW);
+  float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < W; ++w) sum += colrow[w][tid];
-      colout[key] = sum;
-    }
-  }
+  for (int w = 0; w < W; ++w) sum += colrow[w][k];
+  if (FULL || tkey0 + k < key1) colout[tkey0 + k] = sum;
 }
 
 template <int D, int NT, int W, bool PIPE>
@@ -647,18 +661,17 @@ up_colsum_kernel(ScoreArgs a) {
   load_q<D, NT>(a, s0, qpos0, n_eff, R, g, row0, lane, qf, ipos_unused);
 
   // Output element v of a 32x32 tile in lane l sits at row 8(v/4) + 4(l/32) + v%4.
+  // Row biases are stored in the KV group's row order; rows past R get +inf
+  // (probability 0).
+  const float* brow = a.bias + ((int64_t)req * a.hkv + g) * a.rgqa * a.n_query;
   float bv[NT][16];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int rho = row0 + t * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (rho < R) {
-        const int hl = rho / n_eff, ti = rho - hl * n_eff;
-        bv[t][v] = a.bias[((int64_t)req * a.hq + g * a.rgqa + hl) * a.n_query + ti];
-      } else {
-        bv[t][v] = kPosInf;
-      }
+      const float b = brow[min(rho, R - 1)];
+      bv[t][v] = rho < R ? b : kPosInf;
     }
   }
 
@@ -684,14 +697,19 @@ up_colsum_kernel(ScoreArgs a) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) acc = mfma32(qf[0][s], kf[s], acc);
     }
+    // Tile j's column partials are written during tile j+1, whose compute
+    // hides the LDS reads (colbuf is double-buffered; the ring barrier at
+    // the end of tile j+1 orders them before tile j+2 overwrites the buffer).
     auto step = [&](auto u) {
       constexpr int U = decltype(u)::value;
       ks.fetch_full(it + U + 3, kl[(U + 3) % kRing]);
+      if (it + U > 0)
+        colsum_flush<W, KT, true>(colbuf[(U + 1) & 1], wave, lane, key0 + (it + U - 1) * KT, key1,
+                                  colout);
       colsum_iter<D, NT, W, false, PIPE>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1,
                                          lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
                                          colbuf[U & 1], acc, kf);
       ring_step<Tile, true>();
-      colsum_flush<W, KT>(colbuf[U & 1], tid, key0 + (it + U) * KT, key1, colout);
     };
     for (; it + kRing <= nmain; it += kRing) {
       step(std::integral_constant<int, 0>{});
@@ -701,22 +719,29 @@ up_colsum_kernel(ScoreArgs a) {
     }
     for (; it < nfast; ++it) {
       if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+      if (it > 0)
+        colsum_flush<W, KT, false>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT, key1,
+                                   colout);
       colsum_iter<D, NT, W, false, PIPE>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1,
                                          lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
                                          colbuf[it & 1], acc, kf);
       if (it + 3 < ntiles) ring_step<Tile, true>(); else ring_step<Tile, false>();
-      colsum_flush<W, KT>(colbuf[it & 1], tid, key0 + it * KT, key1, colout);
     }
   }
   for (; it < ntiles; ++it) {
     if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+    if (it > 0)
+      colsum_flush<W, KT, false>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT, key1,
+                                 colout);
     f32x16_t acc = {};
     colsum_iter<D, NT, W, true, false>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1,
                                        lane, wave, row0, R, n_eff, qpos0, C, qf, bv, colbuf[it & 1],
                                        acc, kf);
     ring_step<Tile, false>();
-    colsum_flush<W, KT>(colbuf[it & 1], tid, key0 + it * KT, key1, colout);
   }
+  // the last tile (ntiles >= 1: the chunk holds at least one key)
+  colsum_flush<W, KT, false>(colbuf[(ntiles - 1) & 1], wave, lane, key0 + (ntiles - 1) * KT, key1,
+                             colout);
 }
 
 // ---------------------------------------------------------------------------
