@@ -21,7 +21,7 @@
 //     L2 on every publish and poll.  The last workgroup to finish (a done
 //     counter) clears the status words and both counters, so the next call
 //     starts from a clean workspace without a separate clearing launch.
-//   up_compact_copy_kernel   one workgroup per (block, 64 KiB piece): a kept
+//   up_compact_copy_kernel   one workgroup per (block, 32 KiB piece): a kept
 //     block is a run of G consecutive rows, copied as one flat byte range with
 //     16-byte non-temporal loads and stores; dropped rows are never read.
 // Splitting the gather from the scan lets the copy use small, uniform work
@@ -35,7 +35,13 @@ namespace {
 constexpr int kCompactThreads = 256;
 constexpr int kScanPerThread = 4;
 constexpr int kScanTileBlocks = kCompactThreads * kScanPerThread;  // blocks per scan tile
-constexpr int64_t kPieceBytes = 64 << 10;                          // bytes per copy work item
+#ifndef UP_PIECE_KIB
+#define UP_PIECE_KIB 32
+#endif
+#ifndef UP_COPY_UNROLL
+#define UP_COPY_UNROLL 4
+#endif
+constexpr int64_t kPieceBytes = (int64_t)UP_PIECE_KIB << 10;       // bytes per copy work item
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
@@ -65,8 +71,9 @@ struct CompactArgs {
   uint32_t* ctl;      // [0] tile ticket, [1] done counter, [2] sticky look-back timeout flag
   BlockCopy* desc;    // [num_blocks]
   int64_t row_bytes, row_stride, capacity, num_blocks, num_tiles;
-  int64_t pieces;     // copy work items per block
-  int64_t piece_rows; // rows per work item when rows are strided
+  int64_t pieces;      // copy work items per block
+  int64_t piece_bytes; // bytes per work item when rows are packed
+  int64_t piece_rows;  // rows per work item when rows are strided
   int num_seqs, block;
 };
 
@@ -236,7 +243,7 @@ template <int VW>
 __device__ __forceinline__ void copy_flat(char* __restrict__ dst, const char* __restrict__ src,
                                           int64_t nbytes) {
   typedef typename Vec<VW>::T V;
-  constexpr int U = 4;
+  constexpr int U = UP_COPY_UNROLL;
   const V* s = reinterpret_cast<const V*>(src);
   V* d = reinterpret_cast<V*>(dst);
   const int64_t n = nbytes / VW;
@@ -266,21 +273,30 @@ __device__ __forceinline__ void copy_rows(char* __restrict__ dst, const char* __
   }
 }
 
-// Work item w = (block w / pieces, piece w % pieces); a grid-stride loop
-// covers grids capped below the launch limit.
+// Work item w = (block w / pieces, piece w % pieces): consecutive workgroups
+// copy consecutive pieces of one block, so the streams stay sequential in
+// memory.  A grid-stride loop covers batches with more items than one grid.
 template <int VW>
 __global__ void __launch_bounds__(kCompactThreads) up_compact_copy_kernel(CompactArgs a) {
   const int64_t items = a.num_blocks * a.pieces;
   for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
-    const int64_t b = w / a.pieces, piece = w - b * a.pieces;
+    int64_t b, piece;
+    if (items <= 0xffffffffll) {  // 32-bit division where it suffices
+      const uint32_t q = (uint32_t)w / (uint32_t)a.pieces;
+      b = q;
+      piece = (uint32_t)w - q * (uint32_t)a.pieces;
+    } else {
+      b = w / a.pieces;
+      piece = w - b * a.pieces;
+    }
     const BlockCopy d = a.desc[b];
     if (d.dst < 0) continue;  // uniform over the workgroup
     if (a.row_stride == a.row_bytes) {
       const int64_t bytes = (int64_t)d.rows * a.row_bytes;
-      const int64_t p0 = piece * kPieceBytes;
+      const int64_t p0 = piece * a.piece_bytes;
       if (p0 < bytes)
         copy_flat<VW>(a.hidden_out + d.dst * a.row_bytes + p0, a.hidden + d.src * a.row_bytes + p0,
-                      min(kPieceBytes, bytes - p0));
+                      min(a.piece_bytes, bytes - p0));
     } else {
       const int64_t r0 = piece * a.piece_rows;
       if (r0 < d.rows)
@@ -442,9 +458,16 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   a.num_blocks = lay.blocks;
   a.num_tiles = lay.tiles;
   if (row_stride_bytes == row_bytes) {
-    a.pieces = up::ceil_div((int64_t)block * row_bytes, up::kPieceBytes);
+    // kPieceBytes pieces, larger (4 KiB multiples) if a block would need more
+    // than 65535 of them (keeps the item count of huge rows bounded)
+    const int64_t bb = (int64_t)block * row_bytes;
+    a.piece_bytes = up::kPieceBytes;
+    if (up::ceil_div(bb, a.piece_bytes) > 65535)
+      a.piece_bytes = (int64_t)up::align_up((size_t)up::ceil_div(bb, 65535), 4096);
+    a.pieces = up::ceil_div(bb, a.piece_bytes);
     a.piece_rows = block;
   } else {
+    a.piece_bytes = 0;
     a.piece_rows = row_bytes >= up::kPieceBytes ? 1 : up::kPieceBytes / row_bytes;
     if (a.piece_rows > block) a.piece_rows = block;
     a.pieces = up::ceil_div(block, a.piece_rows);
