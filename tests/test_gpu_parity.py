@@ -70,6 +70,16 @@ def test_n_and_block_sweep(n, G):
     _end_to_end(W.make_inputs(w), n, G, name=w.name)
 
 
+@pytest.mark.parametrize("n,G,d", [(4096, 64, 128), (700, 16, 64), (96, 256, 128)])
+def test_large_n_and_head_dims(n, G, d):
+    """n up to the 4096 limit (requests shorter and longer than n), with the
+    64- and 128-wide head paths, G at both ends of its range."""
+    w = W.Workload(name=f"n{n}_G{G}_d{d}", lengths=(4200, 300, 5200), hq=4, hkv=2, head_dim=d,
+                   hidden_dim=64, hidden_dtype="bf16", seed=5500 + n + G + d, plant_frac=0.02,
+                   n_query=n, block=G, num_seqs=3)
+    _end_to_end(W.make_inputs(w), n, G, name=w.name)
+
+
 def test_tail_equals_n_and_small_p():
     w = W.Workload(name="p_sweep", lengths=(4096, 2000), hq=8, hkv=2, head_dim=128, hidden_dim=32,
                    hidden_dtype="bf16", seed=6001, plant_frac=0.1, num_seqs=2)
@@ -160,10 +170,13 @@ def test_select_isolated():
 
 @pytest.mark.parametrize("dtype,dim,strided", [
     (torch.bfloat16, 4096, False), (torch.float32, 512, False), (torch.bfloat16, 96, True),
-    (torch.uint8, 6, False), (torch.float16, 3, True), (torch.int32, 5, False)])
+    (torch.uint8, 6, False), (torch.float16, 3, True), (torch.int32, 5, False),
+    (torch.float32, 2, False), (torch.bfloat16, 4104, False), (torch.bfloat16, 20000, True)])
 def test_compact_isolated(dtype, dim, strided):
     """Compaction alone on random masks, any dtype and row size (16/8/4/1-byte
-    vector paths), packed or strided rows, positions with gaps."""
+    vector paths), packed or strided rows, positions with gaps; blocks whose
+    bytes are not a whole number of copy pieces, and strided rows larger than
+    a piece (one row per work item)."""
     dev = torch.device("cuda")
     lens = [0, 3, 64, 65, 1000, 0, 2049, 130]
     G = 32
