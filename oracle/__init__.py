@@ -23,6 +23,7 @@ from .uniprefill_oracle import (  # noqa: F401
     band_blocks,
     token_keep,
     compact,
+    scatter_back,
     history_new,
     history_append,
     history_kv_len,

@@ -286,6 +286,26 @@ def compact(mask: np.ndarray, hidden: np.ndarray, positions: np.ndarray,
     return hidden[idx], positions[idx], np.asarray(cu_out, dtype=np.int64)
 
 
+def scatter_back(mask: np.ndarray, packed: np.ndarray, full: np.ndarray,
+                 cu_seqlens: Sequence[int], G: int) -> np.ndarray:
+    """Revival (§二 step 3: dropped tokens are frozen, kept aside so that they
+    can be brought back when needed).  Reading: the kept rows, packed in
+    original order as compaction produced them (possibly updated by later
+    layers since), are written back to their own rows of the full-length
+    buffer; rows of dropped blocks keep their frozen contents.  Returns the
+    new full buffer; the arguments are not modified."""
+    cub = block_offsets(cu_seqlens, G)
+    out = full.copy()
+    r = 0
+    for b in range(len(cu_seqlens) - 1):
+        s0, s1 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        for j in range(s1 - s0):
+            if mask[cub[b] + j // G]:
+                out[s0 + j] = packed[r]
+                r += 1
+    return out
+
+
 def history_new(num_seqs: int) -> List[list]:
     """Empty drop-history ledger: one list of (layer_id, kept) per request."""
     return [[] for _ in range(num_seqs)]

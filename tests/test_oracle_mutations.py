@@ -40,6 +40,12 @@ MUTATIONS = {
     "kept_tokens_full_blocks": ("kept[b] += min(blk * G + G, L) - blk * G", "kept[b] += G"),
     "history_cumulative": ("int(cu_out[b + 1]) - int(cu_out[b])", "int(cu_out[b + 1])"),
     "kv_len_strict": ("if lid <= layer and", "if lid < layer and"),
+    "kv_len_first_not_latest": ("(best is None or lid >= best[0])", "(best is None)"),
+    "revival_global_block_index": ("if mask[cub[b] + j // G]:\n                out[s0 + j]",
+                                   "if mask[(s0 + j) // G]:\n                out[s0 + j]"),
+    "revival_row_not_advanced": ("out[s0 + j] = packed[r]\n                r += 1",
+                                 "out[s0 + j] = packed[r]"),
+    "revival_local_row": ("out[s0 + j] = packed[r]", "out[j] = packed[r]"),
 }
 
 

@@ -364,6 +364,36 @@ def check_compaction():
     np.testing.assert_array_equal(c2, cu)
 
 
+def check_revival():
+    """Revival undoes compaction: scattering the packed kept rows back over the
+    original buffer gives the original buffer; over any other buffer it gives
+    the kept rows in their own places and that buffer's rows elsewhere.  A
+    hand example fixes the order: G=2, one request of 5 tokens, blocks
+    {0,1}, {2,3}, {4} with mask 1, 0, 1 -> packed rows p0, p1, p2 land in rows
+    0, 1 and 4."""
+    base = np.array([[10.0], [11.0], [12.0], [13.0], [14.0]])
+    packed = np.array([[0.5], [1.5], [2.5]])
+    out = O.scatter_back(np.array([1, 0, 1], dtype=np.uint8), packed, base, [0, 5], 2)
+    np.testing.assert_array_equal(out[:, 0], [0.5, 1.5, 12.0, 13.0, 2.5])
+    np.testing.assert_array_equal(base[:, 0], [10.0, 11.0, 12.0, 13.0, 14.0])  # input untouched
+    rng = np.random.default_rng(7)
+    lengths = [130, 0, 64, 200, 1, 33]
+    G = 32
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    cub = O.block_offsets(cu, G)
+    T = int(cu[-1])
+    x = rng.integers(0, 2 ** 16, size=(T, 5), dtype=np.uint16)
+    other = rng.integers(0, 2 ** 16, size=(T, 5), dtype=np.uint16)
+    pos = np.zeros(T, dtype=np.int32)
+    for frac in (0.0, 0.5, 1.0):
+        mask = (rng.random(int(cub[-1])) < frac).astype(np.uint8)
+        h_out, _, _ = O.compact(mask, x, pos, cu, G)
+        np.testing.assert_array_equal(O.scatter_back(mask, h_out, x, cu, G), x)
+        keep = O.token_keep(mask, cu, G).astype(bool)
+        np.testing.assert_array_equal(O.scatter_back(mask, h_out, other, cu, G),
+                                      np.where(keep[:, None], x, other))
+
+
 def check_history():
     """Ledger invariants: one entry per request per call, in call order; the
     KV length a layer reads back is the kept count of the latest drop at or
@@ -391,7 +421,7 @@ ALL_CHECKS = [
     check_gqa_peak, check_head_additivity, check_n1_textbook_softmax, check_block_means,
     check_select_golden, check_one_hot, check_uniform_ceil, check_select_invariants,
     check_brute_force, check_scale_invariance, check_concentration, check_short_requests,
-    check_compaction, check_history, check_widen_bf16,
+    check_compaction, check_revival, check_history, check_widen_bf16,
 ]
 
 
