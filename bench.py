@@ -226,6 +226,23 @@ def main():
         step(layer=K + i, marks=brk[i])
     torch.cuda.synchronize()
 
+    # Neighbours of the path, timed outside the timed region: revival (the
+    # packed rows written back over the full buffer; here they are unchanged,
+    # so `hidden` keeps its bytes) and the ledger read-back.
+    kv_len = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    rv_marks = []
+    for i in range(nb):
+        m = new_marks(["up_revive", "up_kv_len"])
+        m["up_revive"][0].record()
+        U.up_revive(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, w.block,
+                    ws.block_mask, ws.hidden_out, hidden, ws.compact_ws)
+        m["up_revive"][1].record()
+        m["up_kv_len"][0].record()
+        U.up_kv_len(ledger, B, cap, 1 << 20, batch.cu_seqlens_d, kv_len)
+        m["up_kv_len"][1].record()
+        rv_marks.append(m)
+    torch.cuda.synchronize()
+
     ms_per_step = (t1 - t0) * 1e3 / K
     per_call_us = {n: mean_us(brk, n) for n in calls}
     per_call_us[dominant] = dominant_us
@@ -241,6 +258,7 @@ def main():
     flops_exec = 2.0 * flops_alg                       # exact column sums recompute S once
     row_bytes = hidden[0].numel() * hidden.element_size()
     compact_bytes = 2 * kept * row_bytes + 2 * 4 * kept + N
+    compact_bytes_rv = 2 * kept * row_bytes + N                   # revival moves no positions
     score_bytes = T * w.hkv * w.head_dim * 2 + sum(min(w.n_query, L) for L in lens) * w.hq * w.head_dim * 2
 
     t_score = per_call_us["up_score"] * 1e-6
@@ -288,6 +306,12 @@ def main():
         "select_compact_hbm": {"bytes": int(compact_bytes + 5 * N),
                                "gbs": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9, 1),
                                "frac_of_peak": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9 / PEAK_HBM_GBS, 4)},
+        "revive": {"us": round(mean_us(rv_marks, "up_revive"), 2),
+                   "gbs": round(compact_bytes_rv / (mean_us(rv_marks, "up_revive") * 1e-6) / 1e9, 1),
+                   "frac_of_hbm_peak": round(compact_bytes_rv / (mean_us(rv_marks, "up_revive") * 1e-6)
+                                             / 1e9 / PEAK_HBM_GBS, 4),
+                   "algorithmic_bytes": int(compact_bytes_rv)},
+        "kv_len_us": round(mean_us(rv_marks, "up_kv_len"), 2),
         "keep_ratio": round(kept / T, 5),
         "input_generation_s": round(t_gen, 2),
     }

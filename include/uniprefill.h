@@ -12,6 +12,9 @@
  *   up_select_topp  Top-p block mask with forced sink / tail blocks
  *   up_compact      gather of the kept rows + positions, new cu_seqlens
  *   up_drop_history append (layer id, kept tokens) to each request's ledger
+ * and, around it,
+ *   up_kv_len       per-layer KV length read back from the ledger
+ *   up_revive       scatter of packed kept rows back into the full buffer
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -212,7 +215,8 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
 
 /*
  * Ledger layout (int32 words, device memory):
- *   [0] status bits (bit 0: an append found a request's record full)
+ *   [0] status bits (bit 0: an append found a request's record full;
+ *       bit 1: a call found a ledger set up for another num_seqs/capacity)
  *   [1] num_seqs   [2] capacity   [3] reserved
  *   [4 + r]                          entries used by request r
  *   [4 + B + 2*(r*capacity + e)]     entry e of request r: layer id
@@ -231,6 +235,48 @@ up_status up_history_init(void* ledger, int num_seqs, int capacity, hipStream_t 
  */
 up_status up_drop_history(void* ledger, int num_seqs, int capacity, int layer_id,
                           const int32_t* cu_seqlens_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Consumers of the ledger and of the frozen rows (§三, §二 step 3)            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * up_kv_len — KV length of every request for layer layer_id, read back from
+ * the ledger (§三: at generation time the ledger tells each layer how many
+ * cache entries it holds).  Reading: a drop at layer l already applies to
+ * layer l, so kv_len[r] is the kept count of the latest-appended entry of
+ * request r whose layer id is <= layer_id, else the prompt length
+ * cu_seqlens[r+1] - cu_seqlens[r].
+ * ledger        as written by up_history_init / up_drop_history (status bit
+ *               1 is set, and prompt lengths written, if its num_seqs or
+ *               capacity differ from the arguments).
+ * cu_seqlens_d  device int32 [B+1], the prompt packing.
+ * kv_len        device int32 [B] (written).
+ */
+up_status up_kv_len(void* ledger, int num_seqs, int capacity, int layer_id,
+                    const int32_t* cu_seqlens_d, int32_t* kv_len, hipStream_t stream);
+
+/*
+ * up_revive — revival of frozen tokens (§二 step 3: dropped tokens are kept
+ * aside, frozen, so they can be brought back).  The inverse of up_compact's
+ * gather for the same mask: row i of `packed` (the i-th kept token in
+ * request-then-token order, as up_compact wrote it, possibly updated since)
+ * is written to its own row of `full`; rows of dropped blocks keep their
+ * (frozen) contents, so `full` holds a complete sequence again.
+ * block, block_mask, cu_*  as for up_compact.
+ * packed     [kept rows, row_bytes] contiguous (read); must not overlap full.
+ * full       [T rows], row t at full + t*row_stride_bytes, row_bytes bytes
+ *            each (kept rows written in place).
+ * workspace  a prepared up_compact workspace of at least
+ *            up_compact_workspace_size bytes; calls sharing it run one at a
+ *            time (it is left prepared again).
+ * Two launches: up_compact's scan (without cu_seqlens_out) and its copy
+ * kernel with source and destination swapped.
+ */
+up_status up_revive(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                    const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                    const void* packed, void* full, int64_t row_bytes, int64_t row_stride_bytes,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

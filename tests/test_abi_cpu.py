@@ -129,3 +129,26 @@ def test_history_rejects_bad_arguments():
     assert lib.up_history_init(16, 2, 0, None) == 1
     assert lib.up_drop_history(16, 2, 4, 0, None, None) == 1
     assert lib.up_history_bytes(-1, 4) == 0
+
+
+def test_revive_rejects_bad_arguments():
+    lib = U.lib()
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    # num_seqs, cu_h, cu_d, cu_blocks_d, block, mask, packed, full, row_bytes, row_stride, ws,
+    # ws_bytes, stream
+    base = [1, cu.data_ptr(), 16, 16, 64, 16, 4096, 8192, 512, 512, 256, 1 << 20, None]
+    cases = [((4, 0), 1, "block"), ((9, 256), 1, "row_stride"), ((8, 0), 1, "row_bytes"),
+             ((11, 16), 3, "workspace"), ((6, None), 1, "NULL"), ((10, 300), 1, "256-byte")]
+    for (i, v), status, msg in cases:
+        a = list(base)
+        a[i] = v
+        st = lib.up_revive(*a)
+        assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())
+
+
+def test_kv_len_rejects_bad_arguments():
+    lib = U.lib()
+    assert lib.up_kv_len(None, 2, 4, 0, 16, 16, None) == 1
+    assert lib.up_kv_len(16, 2, 0, 0, 16, 16, None) == 1
+    assert lib.up_kv_len(16, 2, 4, 0, None, 16, None) == 1
+    assert lib.up_kv_len(16, 0, 4, 0, None, None, None) == 0   # no requests: nothing to do

@@ -252,6 +252,96 @@ def test_history_appends_and_overflow():
     assert led.cpu().numpy()[0] & 2                      # shape mismatch flagged, nothing written
 
 
+def test_kv_len_read_back():
+    """Ledger read-back: per request and layer, the kept count of the latest
+    drop at or below the layer, else the prompt length (oracle history_kv_len);
+    a ledger of another shape is flagged and gives prompt lengths."""
+    dev = torch.device("cuda")
+    cu = [0, 100, 100, 350, 351]
+    B, cap = 4, 4
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+    led = torch.empty(U.up_history_bytes(B, cap) // 4, dtype=torch.int32, device=dev)
+    U.up_history_init(led, B, cap)
+    ref = O.history_new(B)
+    for layer, cu_out in [(2, [0, 90, 90, 300, 301]), (5, [0, 64, 64, 200, 201]),
+                          (5, [0, 60, 60, 180, 181]), (9, [0, 10, 10, 20, 21])]:
+        U.up_drop_history(led, B, cap, layer, torch.tensor(cu_out, dtype=torch.int32, device=dev))
+        O.history_append(ref, layer, cu_out)
+    kv = torch.empty(B, dtype=torch.int32, device=dev)
+    for layer in (0, 1, 2, 4, 5, 8, 9, 1000, -3):
+        U.up_kv_len(led, B, cap, layer, cu_d, kv)
+        torch.cuda.synchronize()
+        exp = [O.history_kv_len(ref[r], layer, cu[r + 1] - cu[r]) for r in range(B)]
+        assert kv.cpu().tolist() == exp, (layer, kv.cpu().tolist(), exp)
+    assert led.cpu().numpy()[0] == 0
+    kv.fill_(-1)
+    U.up_kv_len(led, 3, cap, 5, cu_d, kv)   # wrong num_seqs for this ledger
+    torch.cuda.synchronize()
+    assert kv.cpu().tolist()[:3] == [100, 0, 250] and led.cpu().numpy()[0] & 2
+    # long records (more entries than a wave has lanes), layer ids out of order
+    B2, cap2 = 2, 150
+    cu2 = [0, 5000, 7000]
+    led2 = torch.empty(U.up_history_bytes(B2, cap2) // 4, dtype=torch.int32, device=dev)
+    U.up_history_init(led2, B2, cap2)
+    ref2 = O.history_new(B2)
+    for i in range(130):
+        layer = (i * 37) % 91 - 5
+        cu_out = [0, 4000 - i, 6000 - 3 * i]
+        U.up_drop_history(led2, B2, cap2, layer, torch.tensor(cu_out, dtype=torch.int32, device=dev))
+        O.history_append(ref2, layer, cu_out)
+    kv2 = torch.empty(B2, dtype=torch.int32, device=dev)
+    cu2_d = torch.tensor(cu2, dtype=torch.int32, device=dev)
+    for layer in (-10, -5, 0, 17, 44, 85, 86, 200):
+        U.up_kv_len(led2, B2, cap2, layer, cu2_d, kv2)
+        torch.cuda.synchronize()
+        exp = [O.history_kv_len(ref2[r], layer, cu2[r + 1] - cu2[r]) for r in range(B2)]
+        assert kv2.cpu().tolist() == exp, (layer, kv2.cpu().tolist(), exp)
+
+
+@pytest.mark.parametrize("dtype,dim,strided", [
+    (torch.bfloat16, 4096, False), (torch.float32, 512, False), (torch.bfloat16, 96, True),
+    (torch.uint8, 6, False), (torch.int32, 5, True), (torch.bfloat16, 20000, True)])
+def test_revive(dtype, dim, strided):
+    """Revival (scatter-back) against the oracle: compact, change the packed
+    rows, write them back over a copy of the full buffer; kept rows take the
+    new values, dropped rows keep their frozen contents, byte for byte."""
+    dev = torch.device("cuda")
+    lens = [0, 3, 64, 65, 1000, 0, 2049, 130]
+    G = 32
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    batch = U.Batch.make(cu, G, dev)
+    T = batch.num_tokens
+    gen = torch.Generator().manual_seed(dim + 1)
+    base = torch.randint(-100, 100, (T, dim + (7 if strided else 0)), generator=gen)
+    full0 = base.to(dtype).to(dev)
+    if strided:
+        full0 = full0[:, :dim]
+    ws = U.new_compact_workspace(batch.cu_seqlens_h, G, dev)
+    for frac in (0.0, 0.3, 1.0):
+        mask_np = (torch.rand(batch.num_blocks, generator=gen) < frac).numpy().astype(np.uint8)
+        mask = torch.from_numpy(mask_np).to(dev)
+        packed = torch.zeros((T, dim), dtype=dtype, device=dev)
+        cu_out = torch.empty(len(lens) + 1, dtype=torch.int32, device=dev)
+        U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, full0, None,
+                     packed, None, cu_out, ws)
+        n = int(O.token_keep(mask_np, cu.numpy(), G).sum())
+        # "updated" rows (at least one row: the buffer must exist even when nothing is kept)
+        packed_new = (packed[:max(n, 1)].view(torch.uint8) ^ 0x5A).view(dtype).contiguous()
+        full = full0.clone() if not strided else base.to(dtype).to(dev)[:, :dim]
+        full_before = full.contiguous().view(torch.uint8).cpu().numpy().copy()
+        U.up_revive(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, packed_new,
+                    full, ws)
+        torch.cuda.synchronize()
+        exp = O.scatter_back(mask_np, packed_new[:n].contiguous().view(torch.uint8).cpu().numpy(),
+                             full_before, cu.numpy(), G)
+        got = full.contiguous().view(torch.uint8).cpu().numpy()
+        assert np.array_equal(got, exp), frac
+        if strided:   # bytes between rows are never written
+            whole = full.as_strided((T, dim + 7), (dim + 7, 1))
+            assert torch.equal(whole[:, dim:].cpu(), base.to(dtype)[:, dim:])
+        assert not ws.view(torch.int32)[:2].any()
+
+
 def test_determinism():
     w = W.Workload(name="det", lengths=(20000, 3000), hq=32, hkv=8, head_dim=128, hidden_dim=256,
                    hidden_dtype="bf16", seed=6400, plant_frac=0.05, num_seqs=2)

@@ -23,7 +23,7 @@ __all__ = [
     "up_abi_version", "up_last_error", "up_make_cu_blocks",
     "up_score_workspace_size", "up_score", "up_select_topp",
     "up_compact_workspace_size", "up_compact_workspace_init", "up_compact",
-    "up_history_bytes", "up_history_init", "up_drop_history",
+    "up_history_bytes", "up_history_init", "up_drop_history", "up_kv_len", "up_revive",
     "Batch", "Workspace", "run_chain",
 ]
 
@@ -65,6 +65,8 @@ _SIGNATURES = {
     "up_history_bytes": (_SZ, [_I, _I]),
     "up_history_init": (_I, [_P, _I, _I, _P]),
     "up_drop_history": (_I, [_P, _I, _I, _I, _P, _P]),
+    "up_kv_len": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "up_revive": (_I, [_I, _P, _P, _P, _I, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
 }
 
 
@@ -225,6 +227,33 @@ def up_drop_history(ledger, num_seqs: int, capacity: int, layer_id: int, cu_seql
     _check("up_drop_history", lib().up_drop_history(_ptr(ledger), num_seqs, capacity, layer_id,
                                                     _ptr(cu_seqlens_out),
                                                     _stream(stream, ledger.device)))
+
+
+def up_kv_len(ledger, num_seqs: int, capacity: int, layer_id: int, cu_seqlens_d, kv_len,
+              stream=None) -> None:
+    """Per-request KV length of layer `layer_id` read back from the ledger (§三)."""
+    _check("up_kv_len", lib().up_kv_len(_ptr(ledger), num_seqs, capacity, layer_id,
+                                        _ptr(cu_seqlens_d), _ptr(kv_len),
+                                        _stream(stream, ledger.device)))
+
+
+def up_revive(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, packed, full,
+              workspace, stream=None) -> None:
+    """Write the packed kept rows back to their rows of `full` (§二 step 3,
+    revival); rows of dropped blocks in `full` keep their contents."""
+    if full.dim() < 1 or (full.dim() > 1 and not full[0].is_contiguous()):
+        raise ValueError("full rows must be contiguous")
+    if packed.dtype != full.dtype:
+        raise ValueError("packed must have full's dtype")
+    if packed.dim() > 1 and not packed.is_contiguous():
+        raise ValueError("packed must be contiguous")
+    cu = _host_i32(cu_seqlens_h)
+    row_bytes = (full[0].numel() if full.dim() > 1 else 1) * full.element_size()
+    row_stride = full.stride(0) * full.element_size()
+    st = lib().up_revive(cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_d), _ptr(cu_blocks_d), block,
+                         _ptr(block_mask), _ptr(packed), _ptr(full), row_bytes, row_stride,
+                         _ptr(workspace), workspace.numel(), _stream(stream, full.device))
+    _check("up_revive", st)
 
 
 # ---------------------------------------------------------------------------

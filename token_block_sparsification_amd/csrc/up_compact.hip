@@ -66,7 +66,7 @@ struct CompactArgs {
   const int32_t* positions;
   char* hidden_out;
   int32_t* positions_out;
-  int32_t* cu_out;
+  int32_t* cu_out;    // NULL: not written (revival)
   uint64_t* flags;    // [num_tiles] scan tile status words
   uint32_t* ctl;      // [0] tile ticket, [1] done counter, [2] sticky look-back timeout flag
   BlockCopy* desc;    // [num_blocks]
@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
   __syncthreads();
   const int64_t t = s_tile;
 
-  if (t == 0 && tid == 0) {
+  if (t == 0 && tid == 0 && a.cu_out) {
     // Output packing starts at 0; requests with no blocks before the first
     // block end at 0 as well.
     a.cu_out[0] = 0;
@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
       pos += kept[i];
       // A request whose last block this is (and empty requests right after
       // it) ends at this block's inclusive count.
-      if (b == a.cu_blocks[rq + 1] - 1) {
+      if (a.cu_out && b == a.cu_blocks[rq + 1] - 1) {
         a.cu_out[rq + 1] = (int32_t)pos;
         for (int r2 = rq + 1; r2 < a.num_seqs && a.cu_blocks[r2 + 1] == a.cu_blocks[rq + 1]; ++r2)
           a.cu_out[r2 + 1] = (int32_t)pos;
@@ -258,17 +258,18 @@ __device__ __forceinline__ void copy_flat(char* __restrict__ dst, const char* __
   for (; i < n; i += kCompactThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
 }
 
-// Copy `rows` rows of row_bytes from a strided source to a packed
-// destination, one wave per row.
+// Copy `rows` rows of row_bytes between row layouts with the given strides,
+// one wave per row.
 template <int VW>
-__device__ __forceinline__ void copy_rows(char* __restrict__ dst, const char* __restrict__ src,
-                                          int rows, int64_t row_bytes, int64_t row_stride) {
+__device__ __forceinline__ void copy_rows(char* __restrict__ dst, int64_t dst_stride,
+                                          const char* __restrict__ src, int64_t src_stride, int rows,
+                                          int64_t row_bytes) {
   typedef typename Vec<VW>::T V;
   const int64_t vpr = row_bytes / VW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int r = wave; r < rows; r += kCompactThreads / 64) {
-    const V* s = reinterpret_cast<const V*>(src + (int64_t)r * row_stride);
-    V* d = reinterpret_cast<V*>(dst + (int64_t)r * row_bytes);
+    const V* s = reinterpret_cast<const V*>(src + (int64_t)r * src_stride);
+    V* d = reinterpret_cast<V*>(dst + (int64_t)r * dst_stride);
     for (int64_t c = lane; c < vpr; c += 64) __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
   }
 }
@@ -276,7 +277,10 @@ __device__ __forceinline__ void copy_rows(char* __restrict__ dst, const char* __
 // Work item w = (block w / pieces, piece w % pieces): consecutive workgroups
 // copy consecutive pieces of one block, so the streams stay sequential in
 // memory.  A grid-stride loop covers batches with more items than one grid.
-template <int VW>
+// REVIVE: the same descriptors with source and destination swapped — packed
+// rows (hidden_out side) go back to their own rows of the full buffer
+// (hidden side); positions are not touched.
+template <int VW, bool REVIVE>
 __global__ void __launch_bounds__(kCompactThreads) up_compact_copy_kernel(CompactArgs a) {
   const int64_t items = a.num_blocks * a.pieces;
   for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
@@ -291,20 +295,29 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_copy_kernel(Compac
     }
     const BlockCopy d = a.desc[b];
     if (d.dst < 0) continue;  // uniform over the workgroup
+    char* packed = a.hidden_out + d.dst * a.row_bytes;     // packed side, row_bytes apart
+    char* strided = const_cast<char*>(a.hidden) + d.src * a.row_stride;  // full side
     if (a.row_stride == a.row_bytes) {
       const int64_t bytes = (int64_t)d.rows * a.row_bytes;
       const int64_t p0 = piece * a.piece_bytes;
-      if (p0 < bytes)
-        copy_flat<VW>(a.hidden_out + d.dst * a.row_bytes + p0, a.hidden + d.src * a.row_bytes + p0,
-                      min(a.piece_bytes, bytes - p0));
+      if (p0 < bytes) {
+        const int64_t nb = min(a.piece_bytes, bytes - p0);
+        if (REVIVE) copy_flat<VW>(strided + p0, packed + p0, nb);
+        else copy_flat<VW>(packed + p0, strided + p0, nb);
+      }
     } else {
       const int64_t r0 = piece * a.piece_rows;
-      if (r0 < d.rows)
-        copy_rows<VW>(a.hidden_out + (d.dst + r0) * a.row_bytes,
-                      a.hidden + (d.src + r0) * a.row_stride, (int)min(a.piece_rows, d.rows - r0),
-                      a.row_bytes, a.row_stride);
+      if (r0 < d.rows) {
+        const int nr = (int)min(a.piece_rows, d.rows - r0);
+        if (REVIVE)
+          copy_rows<VW>(strided + r0 * a.row_stride, a.row_stride, packed + r0 * a.row_bytes,
+                        a.row_bytes, nr, a.row_bytes);
+        else
+          copy_rows<VW>(packed + r0 * a.row_bytes, a.row_bytes, strided + r0 * a.row_stride,
+                        a.row_stride, nr, a.row_bytes);
+      }
     }
-    if (a.positions && piece == 0)
+    if (!REVIVE && a.positions && piece == 0)
       for (int i = threadIdx.x; i < d.rows; i += kCompactThreads)
         a.positions_out[d.dst + i] = a.positions[d.src + i];
   }
@@ -346,6 +359,42 @@ __global__ void up_history_append_kernel(int32_t* led, int num_seqs, int capacit
   }
 }
 
+// KV length per request for one layer: the kept count of the latest entry
+// with layer id <= layer, else the prompt length.  One wave per request; lane
+// i looks at entries i, i+64, ...; the wave keeps the largest (layer id,
+// entry index) key among entries at or below the layer.
+__global__ void __launch_bounds__(256) up_kv_len_kernel(const int32_t* led, int num_seqs,
+                                                        int capacity, int layer,
+                                                        const int32_t* cu_seqlens, int32_t* kv_len,
+                                                        int32_t* status) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= num_seqs) return;
+  const int full = cu_seqlens[r + 1] - cu_seqlens[r];
+  if (led[1] != num_seqs || led[2] != capacity) {  // ledger set up for another shape
+    if (lane == 0) {
+      kv_len[r] = full;
+      if (r == 0) atomicOr(status, 2);
+    }
+    return;
+  }
+  const int cnt = min(led[kLedgerHeader + r], capacity);
+  const int32_t* e = led + kLedgerHeader + num_seqs + 2 * (int64_t)r * capacity;
+  uint64_t key = 0;  // 0: no entry at or below the layer
+  for (int i = lane; i < cnt; i += 64) {
+    const int lid = e[2 * i];
+    if (lid <= layer) {
+      const uint64_t k = (1ull << 63) | ((uint64_t)((uint32_t)lid ^ 0x80000000u) << 31) | (uint64_t)i;
+      key = k > key ? k : key;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(key, off);
+    key = o > key ? o : key;
+  }
+  if (lane == 0) kv_len[r] = key ? e[2 * (int)(key & 0x7fffffffu) + 1] : full;
+}
+
 }  // namespace
 
 int compact_tile_blocks(int block) {
@@ -372,6 +421,108 @@ CompactLayout compact_layout(int num_seqs, const int32_t* cu_h, int block) {
   l.off_desc = up::align_up(l.off_flags + (size_t)l.tiles * sizeof(uint64_t), 256);
   l.bytes = up::align_up(l.off_desc + (size_t)l.blocks * sizeof(up::BlockCopy), 256);
   return l;
+}
+
+// Arguments shared by up_compact and up_revive (the revive call passes the
+// full buffer as `hidden` and the packed rows as `hidden_out`).
+struct GatherCall {
+  int num_seqs;
+  const int32_t* cu_h;
+  const int32_t* cu_d;
+  const int32_t* cu_blocks_d;
+  int block;
+  const uint8_t* mask;
+  const void* hidden;
+  int64_t row_bytes, row_stride;
+  const int32_t* positions;
+  void* hidden_out;
+  int32_t* positions_out;
+  int32_t* cu_out;
+  int64_t capacity;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+template <bool REVIVE>
+void launch_copy(const up::CompactArgs& a, dim3 grid, uintptr_t al, hipStream_t stream) {
+  if ((al & 15) == 0)
+    hipLaunchKernelGGL((up::up_compact_copy_kernel<16, REVIVE>), grid, dim3(up::kCompactThreads), 0,
+                       stream, a);
+  else if ((al & 7) == 0)
+    hipLaunchKernelGGL((up::up_compact_copy_kernel<8, REVIVE>), grid, dim3(up::kCompactThreads), 0,
+                       stream, a);
+  else if ((al & 3) == 0)
+    hipLaunchKernelGGL((up::up_compact_copy_kernel<4, REVIVE>), grid, dim3(up::kCompactThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((up::up_compact_copy_kernel<1, REVIVE>), grid, dim3(up::kCompactThreads), 0,
+                       stream, a);
+}
+
+up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
+  if (c.block < 1 || c.block > 4096) return up::set_error(UP_ERR_INVALID, "block not in [1, 4096]");
+  if (c.row_bytes < 1 || c.row_stride < c.row_bytes)
+    return up::set_error(UP_ERR_INVALID, "need row_bytes >= 1 and row_stride_bytes >= row_bytes");
+  if (c.row_bytes > ((int64_t)1 << 30))
+    return up::set_error(UP_ERR_UNSUPPORTED, "row_bytes above 1 GiB");
+  if (!c.cu_d || !c.cu_blocks_d || !c.ws || (T > 0 && !c.mask))
+    return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if ((uintptr_t)c.ws & 255) return up::set_error(UP_ERR_INVALID, "workspace not 256-byte aligned");
+  const CompactLayout lay = compact_layout(c.num_seqs, c.cu_h, c.block);
+  if (c.ws_bytes < lay.bytes)
+    return up::set_error(UP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", c.ws_bytes, lay.bytes);
+  if (c.num_seqs == 0) return UP_OK;
+  up_status st = up::check_device();
+  if (st != UP_OK) return st;
+
+  up::CompactArgs a{};
+  a.cu_seqlens = c.cu_d;
+  a.cu_blocks = c.cu_blocks_d;
+  a.mask = c.mask;
+  a.hidden = static_cast<const char*>(c.hidden);
+  a.positions = c.positions;
+  a.hidden_out = static_cast<char*>(c.hidden_out);
+  a.positions_out = c.positions_out;
+  a.cu_out = c.cu_out;
+  a.ctl = static_cast<uint32_t*>(c.ws);
+  a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(c.ws) + lay.off_flags);
+  a.desc = reinterpret_cast<up::BlockCopy*>(static_cast<char*>(c.ws) + lay.off_desc);
+  a.row_bytes = c.row_bytes;
+  a.row_stride = c.row_stride;
+  a.capacity = c.capacity;
+  a.num_seqs = c.num_seqs;
+  a.block = c.block;
+  a.num_blocks = lay.blocks;
+  a.num_tiles = lay.tiles;
+  if (c.row_stride == c.row_bytes) {
+    // kPieceBytes pieces, larger (4 KiB multiples) if a block would need more
+    // than 65535 of them (keeps the item count of huge rows bounded)
+    const int64_t bb = (int64_t)c.block * c.row_bytes;
+    a.piece_bytes = up::kPieceBytes;
+    if (up::ceil_div(bb, a.piece_bytes) > 65535)
+      a.piece_bytes = (int64_t)up::align_up((size_t)up::ceil_div(bb, 65535), 4096);
+    a.pieces = up::ceil_div(bb, a.piece_bytes);
+    a.piece_rows = c.block;
+  } else {
+    a.piece_bytes = 0;
+    a.piece_rows = c.row_bytes >= up::kPieceBytes ? 1 : up::kPieceBytes / c.row_bytes;
+    if (a.piece_rows > c.block) a.piece_rows = c.block;
+    a.pieces = up::ceil_div(c.block, a.piece_rows);
+  }
+
+  hipLaunchKernelGGL(up::up_compact_scan_kernel, dim3((unsigned)(a.num_tiles > 0 ? a.num_tiles : 1)),
+                     dim3(up::kCompactThreads), 0, c.stream, a);
+  st = up::check_launch("up_compact_scan_kernel");
+  if (st != UP_OK || a.num_blocks == 0) return st;
+
+  const int64_t items = a.num_blocks * a.pieces;
+  const dim3 grid((unsigned)(items < (int64_t)1 << 30 ? items : (int64_t)1 << 30));
+  const uintptr_t al = (uintptr_t)c.hidden | (uintptr_t)c.hidden_out | (uintptr_t)c.row_bytes |
+                       (uintptr_t)c.row_stride;
+  if (revive) launch_copy<true>(a, grid, al, c.stream);
+  else launch_copy<false>(a, grid, al, c.stream);
+  return up::check_launch("up_compact_copy_kernel");
 }
 
 }  // namespace
@@ -415,82 +566,51 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   int max_len;
   up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &max_len);
   if (st != UP_OK) return st;
-  if (block < 1 || block > 4096) return up::set_error(UP_ERR_INVALID, "block not in [1, 4096]");
-  if (row_bytes < 1 || row_stride_bytes < row_bytes)
-    return up::set_error(UP_ERR_INVALID, "need row_bytes >= 1 and row_stride_bytes >= row_bytes");
-  if (row_bytes > ((int64_t)1 << 30))
-    return up::set_error(UP_ERR_UNSUPPORTED, "row_bytes above 1 GiB");
   if (out_capacity_rows < T)
     return up::set_error(UP_ERR_CAPACITY, "out_capacity_rows %lld < T %lld",
                          (long long)out_capacity_rows, (long long)T);
-  if (!cu_seqlens_d || !cu_blocks_d || !cu_seqlens_out || !workspace ||
-      (T > 0 && (!block_mask || !hidden || !hidden_out)))
+  if (!cu_seqlens_out || (T > 0 && (!hidden || !hidden_out)))
     return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
   if ((positions == nullptr) != (positions_out == nullptr))
     return up::set_error(UP_ERR_INVALID, "positions and positions_out must both be set or both NULL");
-  if ((uintptr_t)workspace & 255) return up::set_error(UP_ERR_INVALID, "workspace not 256-byte aligned");
-  size_t need;
-  up_compact_workspace_size(num_seqs, cu_seqlens_h, block, &need);
-  if (workspace_bytes < need)
-    return up::set_error(UP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  if (num_seqs == 0) return UP_OK;
-  st = up::check_device();
+  GatherCall c{num_seqs,  cu_seqlens_h, cu_seqlens_d,     cu_blocks_d, block,
+               block_mask, hidden,      row_bytes,        row_stride_bytes,
+               positions, hidden_out,  positions_out,    cu_seqlens_out, out_capacity_rows,
+               workspace, workspace_bytes, stream};
+  return run_gather(c, T, false);
+}
+
+up_status up_revive(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                    const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                    const void* packed, void* full, int64_t row_bytes, int64_t row_stride_bytes,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  up::clear_error();
+  int64_t T;
+  int max_len;
+  up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &max_len);
   if (st != UP_OK) return st;
+  if (T > 0 && (!packed || !full)) return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  // The full buffer plays the input role of up_compact, the packed rows the
+  // output role; the copy runs the other way.
+  GatherCall c{num_seqs, cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block, block_mask, full,
+               row_bytes, row_stride_bytes, nullptr, const_cast<void*>(packed), nullptr, nullptr,
+               T, workspace, workspace_bytes, stream};
+  return run_gather(c, T, true);
+}
 
-  const CompactLayout lay = compact_layout(num_seqs, cu_seqlens_h, block);
-  up::CompactArgs a{};
-  a.cu_seqlens = cu_seqlens_d;
-  a.cu_blocks = cu_blocks_d;
-  a.mask = block_mask;
-  a.hidden = static_cast<const char*>(hidden);
-  a.positions = positions;
-  a.hidden_out = static_cast<char*>(hidden_out);
-  a.positions_out = positions_out;
-  a.cu_out = cu_seqlens_out;
-  a.ctl = static_cast<uint32_t*>(workspace);
-  a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + lay.off_flags);
-  a.desc = reinterpret_cast<up::BlockCopy*>(static_cast<char*>(workspace) + lay.off_desc);
-  a.row_bytes = row_bytes;
-  a.row_stride = row_stride_bytes;
-  a.capacity = out_capacity_rows;
-  a.num_seqs = num_seqs;
-  a.block = block;
-  a.num_blocks = lay.blocks;
-  a.num_tiles = lay.tiles;
-  if (row_stride_bytes == row_bytes) {
-    // kPieceBytes pieces, larger (4 KiB multiples) if a block would need more
-    // than 65535 of them (keeps the item count of huge rows bounded)
-    const int64_t bb = (int64_t)block * row_bytes;
-    a.piece_bytes = up::kPieceBytes;
-    if (up::ceil_div(bb, a.piece_bytes) > 65535)
-      a.piece_bytes = (int64_t)up::align_up((size_t)up::ceil_div(bb, 65535), 4096);
-    a.pieces = up::ceil_div(bb, a.piece_bytes);
-    a.piece_rows = block;
-  } else {
-    a.piece_bytes = 0;
-    a.piece_rows = row_bytes >= up::kPieceBytes ? 1 : up::kPieceBytes / row_bytes;
-    if (a.piece_rows > block) a.piece_rows = block;
-    a.pieces = up::ceil_div(block, a.piece_rows);
-  }
-
-  hipLaunchKernelGGL(up::up_compact_scan_kernel, dim3((unsigned)(a.num_tiles > 0 ? a.num_tiles : 1)),
-                     dim3(up::kCompactThreads), 0, stream, a);
-  st = up::check_launch("up_compact_scan_kernel");
-  if (st != UP_OK || a.num_blocks == 0) return st;
-
-  const int64_t items = a.num_blocks * a.pieces;
-  const dim3 grid((unsigned)(items < (int64_t)1 << 30 ? items : (int64_t)1 << 30));
-  const uintptr_t al = (uintptr_t)hidden | (uintptr_t)hidden_out | (uintptr_t)row_bytes |
-                       (uintptr_t)row_stride_bytes;
-  if ((al & 15) == 0)
-    hipLaunchKernelGGL(up::up_compact_copy_kernel<16>, grid, dim3(up::kCompactThreads), 0, stream, a);
-  else if ((al & 7) == 0)
-    hipLaunchKernelGGL(up::up_compact_copy_kernel<8>, grid, dim3(up::kCompactThreads), 0, stream, a);
-  else if ((al & 3) == 0)
-    hipLaunchKernelGGL(up::up_compact_copy_kernel<4>, grid, dim3(up::kCompactThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(up::up_compact_copy_kernel<1>, grid, dim3(up::kCompactThreads), 0, stream, a);
-  return up::check_launch("up_compact_copy_kernel");
+up_status up_kv_len(void* ledger, int num_seqs, int capacity, int layer_id,
+                    const int32_t* cu_seqlens_d, int32_t* kv_len, hipStream_t stream) {
+  up::clear_error();
+  if (!ledger || (num_seqs > 0 && (!cu_seqlens_d || !kv_len)))
+    return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if (num_seqs < 0 || capacity < 1) return up::set_error(UP_ERR_INVALID, "need num_seqs >= 0, capacity >= 1");
+  if (num_seqs == 0) return UP_OK;
+  up_status st = up::check_device();
+  if (st != UP_OK) return st;
+  int32_t* led = static_cast<int32_t*>(ledger);
+  hipLaunchKernelGGL(up::up_kv_len_kernel, dim3((unsigned)up::ceil_div(num_seqs, 4)), dim3(256), 0,
+                     stream, led, num_seqs, capacity, layer_id, cu_seqlens_d, kv_len, led);
+  return up::check_launch("up_kv_len_kernel");
 }
 
 size_t up_history_bytes(int num_seqs, int capacity) {
