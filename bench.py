@@ -47,6 +47,12 @@ def parse_args():
                     help="BLAS threads the oracle may use")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference for counter scaling)")
+    ap.add_argument("--stack", action="store_true",
+                    help="instead of the path step, time a synthetic hybrid stack (random weights) "
+                         "with and without pruning and print its own JSON line")
+    ap.add_argument("--stack-top-p", default="0.99,0.9,0.7",
+                    help="comma-separated top_p values for --stack")
+    ap.add_argument("--stack-len", type=int, default=32768, help="tokens of the --stack request")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-probe run into profiles/traffic.json and exit")
@@ -140,6 +146,9 @@ def main():
     U.lib()  # fail loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.stack:
+        stack_bench(args, dev)
+        return
 
     w = W.get_workload(args.workload)
     t_gen = time.perf_counter()
@@ -318,6 +327,63 @@ def main():
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["parity"] = cpu_leg(w, inp, ws, kept, args.cpu_threads, T)
+    print(json.dumps(rec), flush=True)
+
+
+def stack_bench(args, dev):
+    """Synthetic hybrid stack (random weights; token-local MLP layers between
+    full-attention layers): forward time with the pruning path at each
+    full-attention layer vs the same stack carrying every token."""
+    import torch
+
+    from token_block_sparsification_amd.stack import HybridStack, StackConfig
+
+    L = args.stack_len
+    base = StackConfig()
+    g = torch.Generator().manual_seed(123)
+    h = torch.randn(L, base.d_model, generator=g).to(torch.bfloat16).to(dev)
+    cu = torch.tensor([0, L], dtype=torch.int32)
+    pos = torch.arange(L, dtype=torch.int32, device=dev)
+
+    def timed(stack, prune, reps=5):
+        for _ in range(2):
+            stack.forward(h, cu, pos, prune=prune)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            r = stack.forward(h, cu, pos, prune=prune)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), r
+
+    import numpy as np
+    runs = []
+    t_full = None
+    for p in [float(x) for x in args.stack_top_p.split(",")]:
+        cfg = StackConfig(top_p=p)
+        stack = HybridStack(cfg, dev)
+        if t_full is None:
+            t_full, _ = timed(stack, False)
+        t, r = timed(stack, True)
+        runs.append({"top_p": p, "ms": round(t * 1e3, 3), "speedup_vs_unpruned": round(t_full / t, 4),
+                     "tokens_per_layer": r.tokens_per_layer,
+                     "layer_tokens_fraction": round(sum(r.tokens_per_layer) /
+                                                    (L * len(cfg.pattern)), 4)})
+        del stack
+    first = runs[0]
+    rec = {
+        "metric": "synthetic hybrid stack forward tokens/s with pruning at full-attention layers",
+        "value": round(L / (first["ms"] * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": 5, "warmup": 2, "ms_per_step": first["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random weights and embeddings)",
+        "config": {"workload": f"hybrid_stack_L{L}", "pattern": base.pattern, "d_model": base.d_model,
+                   "d_ff": base.d_ff, "hq": base.hq, "hkv": base.hkv, "head_dim": base.head_dim,
+                   "n_query": base.n_query, "block": base.block, "parallelism": "single GPU"},
+        "unpruned_ms": round(t_full * 1e3, 3),
+        "runs": runs,
+    }
     print(json.dumps(rec), flush=True)
 
 
