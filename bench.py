@@ -78,9 +78,15 @@ def load_traffic(kernel: str, src: str, launches_per_call: int = 1):
 
 
 COPY_BYTES = 1 << 30
-TRAFFIC_KERNELS = {"up_compact_copy_kernel": "up_compact.hip", "up_compact_scan_kernel": "up_compact.hip",
-                   "up_rowstats_kernel": "up_score.hip", "up_colsum_kernel": "up_score.hip",
-                   "up_select_kernel": "up_select.hip"}
+# name in traffic.json -> (source file, pattern of the dispatch names it covers)
+TRAFFIC_KERNELS = {
+    "up_compact_copy_kernel": ("up_compact.hip", r"\bup_compact_copy_kernel<\d+, false>"),
+    "up_revive_copy_kernel": ("up_compact.hip", r"\bup_compact_copy_kernel<\d+, true>"),
+    "up_compact_scan_kernel": ("up_compact.hip", r"\bup_compact_scan_kernel\b"),
+    "up_rowstats_kernel": ("up_score.hip", r"\bup_rowstats_kernel\b"),
+    "up_colsum_kernel": ("up_score.hip", r"\bup_colsum_kernel\b"),
+    "up_select_kernel": ("up_select.hip", r"\bup_select_kernel\b"),
+}
 
 
 def write_traffic(fetch_csv: str, write_csv: str) -> None:
@@ -110,8 +116,8 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
         if not copies:
             raise SystemExit(f"no copy kernel in {path}")
         scale = COPY_BYTES / max(copies)
-        for short, src in TRAFFIC_KERNELS.items():
-            vals = [x for n, v in per.items() if re.search(r"\b" + short + r"\b", n) for x in v]
+        for short, (src, pat) in TRAFFIC_KERNELS.items():
+            vals = [x for n, v in per.items() if re.search(pat, n) for x in v]
             if not vals:
                 continue
             rec = out.setdefault(short, {"source_sha": source_sha(src), "source": src})
@@ -319,7 +325,10 @@ def main():
                    "gbs": round(compact_bytes_rv / (mean_us(rv_marks, "up_revive") * 1e-6) / 1e9, 1),
                    "frac_of_hbm_peak": round(compact_bytes_rv / (mean_us(rv_marks, "up_revive") * 1e-6)
                                              / 1e9 / PEAK_HBM_GBS, 4),
-                   "algorithmic_bytes": int(compact_bytes_rv)},
+                   "algorithmic_bytes": int(compact_bytes_rv),
+                   "traffic": (lambda a, b: a + b if a is not None and b is not None else None)(
+                       load_traffic("up_revive_copy_kernel", "up_compact.hip"),
+                       load_traffic("up_compact_scan_kernel", "up_compact.hip"))},
         "kv_len_us": round(mean_us(rv_marks, "up_kv_len"), 2),
         "keep_ratio": round(kept / T, 5),
         "input_generation_s": round(t_gen, 2),
