@@ -52,11 +52,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Copy descriptor of one block: dst < 0 marks a dropped block (or one that
 // would not fit the output capacity).
-struct BlockCopy {
+struct __attribute__((aligned(16))) BlockCopy {
   int64_t dst;  // first output row
   int32_t src;  // first input row
   int32_t rows;
 };
+static_assert(sizeof(BlockCopy) == 16, "descriptor is one 16-byte load");
 
 struct CompactArgs {
   const int32_t* cu_seqlens;
@@ -293,7 +294,13 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_copy_kernel(Compac
       b = w / a.pieces;
       piece = w - b * a.pieces;
     }
-    const BlockCopy d = a.desc[b];
+    // one 16-byte load (the struct's fields would otherwise be fetched by
+    // two dependent loads around the early exit)
+    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(a.desc + b);
+    BlockCopy d;
+    d.dst = (int64_t)(((uint64_t)raw[1] << 32) | raw[0]);
+    d.src = (int32_t)raw[2];
+    d.rows = (int32_t)raw[3];
     if (d.dst < 0) continue;  // uniform over the workgroup
     char* packed = a.hidden_out + d.dst * a.row_bytes;     // packed side, row_bytes apart
     char* strided = const_cast<char*>(a.hidden) + d.src * a.row_stride;  // full side
