@@ -241,6 +241,21 @@ def main():
         step(layer=K + i, marks=brk[i])
     torch.cuda.synchronize()
 
+    # Cold-cache chains: before each, 512 MiB of scratch writes evict K and
+    # the hidden rows from L2 and the Infinity Cache; then one bracketed step.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(nb):
+        flush.fill_(i & 0xFF)
+        m = new_marks(["chain"])
+        m["chain"][0].record()
+        step(layer=K + nb + i)
+        m["chain"][1].record()
+        cold.append(m)
+    torch.cuda.synchronize()
+    cold_us = sorted(m["chain"][0].elapsed_time(m["chain"][1]) * 1e3 for m in cold)
+    del flush
+
     # Neighbours of the path, timed outside the timed region: revival (the
     # packed rows written back over the full buffer; here they are unchanged,
     # so `hidden` keeps its bytes) and the ledger read-back.
@@ -313,6 +328,10 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "breakdown_us": {k2: round(v, 2) for k2, v in per_call_us.items()},
+        "chain_us_cold_cache": {"p10": round(float(np.percentile(cold_us, 10)), 2),
+                                "median": round(float(np.median(cold_us)), 2),
+                                "p90": round(float(np.percentile(cold_us, 90)), 2),
+                                "chains": len(cold_us)},
         "score_mfma": {"executed_tflops": round(score_tflops_exec, 1),
                        "algorithmic_tflops": round(score_tflops_alg, 1),
                        "frac_of_peak_executed": round(score_tflops_exec / PEAK_BF16_TFLOPS, 4),
@@ -415,17 +434,31 @@ def cpu_leg(w, inp, ws, kept, threads, T):
     k64 = O.widen_bf16(inp["k"].view(torch.int16).cpu().numpy())
     hid = inp["hidden"].view(torch.int16).cpu().numpy()
     pos = inp["positions"].cpu().numpy()
+    steps = {}
     with threadpool_limits(threads):
         t0 = time.perf_counter()
-        out = O.run_chain(q64, k64, hid, pos, cu, w.n_query, w.block, w.top_p, w.sink, w.tail)
-        dt = time.perf_counter() - t0
+        c = O.token_scores(q64, k64, cu, w.n_query, None)
+        bsc = O.block_scores(c, cu, w.block)
+        t1 = time.perf_counter()
+        mask, kept_ref = O.select_topp(bsc, cu, w.block, w.top_p, w.sink, w.tail)
+        t2 = time.perf_counter()
+        h_out, p_out, cu_out = O.compact(mask, hid, pos, cu, w.block)
+        t3 = time.perf_counter()
+        led = O.history_new(len(lens))
+        O.history_append(led, 0, cu_out)
+        t4 = time.perf_counter()
+    dt = t4 - t0
+    steps = {"score_s": round(t1 - t0, 3), "select_s": round(t2 - t1, 3),
+             "compact_s": round(t3 - t2, 3), "history_s": round(t4 - t3, 4)}
+    out = {"token_scores": c, "block_scores": bsc, "mask": mask, "hidden_out": h_out,
+           "positions_out": p_out, "cu_out": cu_out}
     try:
         import multiprocessing
         host_cores = multiprocessing.cpu_count()
     except Exception:
         host_cores = None
     cpu = {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-           "seconds": round(dt, 2),
+           "seconds": round(dt, 2), "seconds_per_step": steps,
            "sample": f"the full bench batch ({len(lens)} request(s), {T} tokens): fp64 numpy oracle "
                      f"score+select+compact+history, BLAS limited to {threads} thread(s); "
                      f"host reports {host_cores} logical CPUs"}
