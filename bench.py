@@ -233,6 +233,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dominant_us = mean_us(timed_marks, dominant)
+    dom_all = [m[dominant][0].elapsed_time(m[dominant][1]) * 1e3 for m in timed_marks]
 
     # Per-call breakdown from extra steps outside the timed region.
     nb = min(K, 20)
@@ -328,6 +329,9 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "breakdown_us": {k2: round(v, 2) for k2, v in per_call_us.items()},
+        "dominant_call_us": {"call": dominant, "p10": round(float(np.percentile(dom_all, 10)), 2),
+                             "median": round(float(np.median(dom_all)), 2),
+                             "p90": round(float(np.percentile(dom_all, 90)), 2)},
         "chain_us_cold_cache": {"p10": round(float(np.percentile(cold_us, 10)), 2),
                                 "median": round(float(np.median(cold_us)), 2),
                                 "p90": round(float(np.percentile(cold_us, 90)), 2),

@@ -295,13 +295,21 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Interleave hint for one group: one MFMA then a few VALU ops, D/16 times.
+// Interleave hint for one group: UP_IL_MFMA MFMAs then a few VALU ops,
+// repeated over the group's D/16 MFMAs.
+#ifndef UP_IL_MFMA
+#define UP_IL_MFMA 1
+#endif
+#ifndef UP_IL_VALU
+#define UP_IL_VALU 64
+#endif
 template <int D>
 __device__ __forceinline__ void interleave_hint() {
+  constexpr int kSlots = D / 16 / UP_IL_MFMA;
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x402, 64 / (D / 16), 0);    // VALU or TRANS
+  for (int i = 0; i < kSlots; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, UP_IL_MFMA, 0);          // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x402, UP_IL_VALU / kSlots, 0);  // VALU or TRANS
   }
 }
 
