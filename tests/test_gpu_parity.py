@@ -139,6 +139,43 @@ def test_head_split_additivity():
     assert rel < 1e-5, rel
 
 
+def test_fused_qkv_and_head_major_strides():
+    """Q and K read in place from a fused [T, (Hq + 2 Hkv) * d] QKV buffer, and
+    from a head-major [H, T, d] layout: the same bits as contiguous inputs."""
+    dev = torch.device("cuda")
+    w = W.Workload(name="strides", lengths=(1500, 77, 2300), hq=8, hkv=2, head_dim=128,
+                   hidden_dim=16, hidden_dtype="bf16", seed=7001, plant_frac=0.05, num_seqs=3)
+    inp = W.make_inputs(w, nan_fill_q=False)
+    batch = U.Batch.make(inp["cu_seqlens"], w.block, dev)
+    T, d, hq, hkv = batch.num_tokens, w.head_dim, w.hq, w.hkv
+    q = inp["q"].to(dev)
+    k = inp["k"].to(dev)
+
+    def score(qq, kk):
+        ws = torch.empty(U.up_score_workspace_size(batch.cu_seqlens_h, hq, hkv, d, w.n_query),
+                         dtype=torch.uint8, device=dev)
+        ts = torch.empty(T, device=dev)
+        bs = torch.empty(batch.num_blocks, device=dev)
+        U.up_score(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, qq, kk, w.n_query,
+                   w.block, 0.0, ts, bs, ws)
+        return ts, bs
+
+    ts0, bs0 = score(q, k)
+    qkv = torch.empty(T, (hq + 2 * hkv) * d, dtype=torch.bfloat16, device=dev)
+    qkv[:, :hq * d] = q.reshape(T, -1)
+    qkv[:, hq * d:(hq + hkv) * d] = k.reshape(T, -1)
+    qkv[:, (hq + hkv) * d:] = float("nan")   # V: never read
+    ts1, bs1 = score(qkv[:, :hq * d].view(T, hq, d), qkv[:, hq * d:(hq + hkv) * d].view(T, hkv, d))
+    qh = q.transpose(0, 1).contiguous().transpose(0, 1)    # storage [hq, T, d]
+    kh = k.transpose(0, 1).contiguous().transpose(0, 1)
+    ts2, bs2 = score(qh, kh)
+    torch.cuda.synchronize()
+    assert torch.equal(ts0, ts1) and torch.equal(bs0, bs1)
+    assert torch.equal(ts0, ts2) and torch.equal(bs0, bs2)
+    c_ref, _ = oracle_scores(inp, w.n_query, w.block)
+    check_scores(ts0.double().cpu().numpy(), c_ref, inp["cu_seqlens"].numpy(), "token scores")
+
+
 def test_select_isolated():
     """Selection alone on given fp32 scores (incl. exact ties, one-hot, zeros
     and 100000 blocks in one request): masks and kept counts must equal the
