@@ -24,6 +24,10 @@ from .uniprefill_oracle import (  # noqa: F401
     token_keep,
     compact,
     scatter_back,
+    round_to_format,
+    rms_normalize,
+    compact_rmsnorm,
+    gather_add,
     history_new,
     history_append,
     history_kv_len,

@@ -306,6 +306,73 @@ def scatter_back(mask: np.ndarray, packed: np.ndarray, full: np.ndarray,
     return out
 
 
+# ---------------------------------------------------------------------------
+# Fused pipeline: the next layer reads the kept rows itself
+# ---------------------------------------------------------------------------
+#
+# §二 step 3 says the later layers work on the kept tokens only while the
+# dropped tokens' states stay frozen.  The consumer of the kept rows is the
+# next layer, whose input passes through an RMS normalisation (pre-norm) and
+# whose output is added back onto the residual stream.  Reading taken: with
+# the gather folded into those two reads, the next layer's normalised operand
+# and its residual sum are the same numbers as normalising / adding the
+# compacted rows, so the oracle states them as compaction followed by the
+# plain definition of each operation.
+
+# (significant bits, smallest normal exponent, largest exponent) per format
+_FORMATS = {"bf16": (8, -126, 127), "f16": (11, -14, 15), "f32": (24, -126, 127)}
+
+
+def round_to_format(x, fmt: str) -> np.ndarray:
+    """Nearest value of a binary floating-point format for every element of
+    the fp64 array x, ties to even, subnormals kept, overflow to infinity
+    (IEEE 754 round-to-nearest-even); returned as fp64.  fmt is "bf16"
+    (8 significant bits), "f16" (11) or "f32" (24)."""
+    p, emin, emax = _FORMATS[fmt]
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                       # |x| in [2^(e-1), 2^e)
+    q = np.maximum(e - p, emin - p + 1)      # exponent of the last kept bit
+    y = np.ldexp(np.round(np.ldexp(x, -q)), q)  # np.round: half to even
+    top = (2.0 - 2.0 ** (1 - p)) * 2.0 ** emax
+    return np.where(np.abs(y) > top, np.copysign(np.inf, x), y)
+
+
+def rms_normalize(rows: np.ndarray, gamma: Optional[np.ndarray], eps: float) -> np.ndarray:
+    """RMS normalisation of each row in fp64: y = x / sqrt(mean(x^2) + eps),
+    times the per-column gain gamma when one is given."""
+    rows = np.asarray(rows, dtype=np.float64)
+    ms = (rows * rows).sum(axis=1, keepdims=True) / rows.shape[1]
+    y = rows / np.sqrt(ms + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)[None, :]
+    return y
+
+
+def compact_rmsnorm(mask: np.ndarray, hidden: np.ndarray, positions: np.ndarray,
+                    cu_seqlens: Sequence[int], G: int, gamma: Optional[np.ndarray], eps: float):
+    """The next layer's normalised operand, read straight from the frozen
+    rows: the kept rows in order (compact), each RMS-normalised in fp64.
+    Returns (normalised rows fp64 before rounding, positions_out,
+    cu_seqlens_out); round_to_format gives the stored values."""
+    h, p_out, cu_out = compact(mask, hidden, positions, cu_seqlens, G)
+    return rms_normalize(h, gamma, eps), p_out, cu_out
+
+
+def gather_add(mask: np.ndarray, frozen: np.ndarray, delta: np.ndarray,
+               cu_seqlens: Sequence[int], G: int, fmt: str) -> np.ndarray:
+    """The next layer's residual sum, reading the residual from the frozen
+    rows: out[i] = frozen[i-th kept row] + delta[i], rounded once to fmt.
+    Inputs are fp64 arrays holding values of fmt; their fp64 sum is rounded
+    to nearest-even.  (A kernel that adds in fp32 and then rounds to bf16 or
+    f16 gets the same values: fp32 carries at least 2p + 2 bits for those
+    formats, so the second rounding is innocuous.)"""
+    T = int(cu_seqlens[-1])
+    h, _, _ = compact(mask, np.asarray(frozen, dtype=np.float64), np.zeros(T, dtype=np.int32),
+                      cu_seqlens, G)
+    d = np.asarray(delta, dtype=np.float64)[: len(h)]
+    return round_to_format(h + d, fmt)
+
+
 def history_new(num_seqs: int) -> List[list]:
     """Empty drop-history ledger: one list of (layer_id, kept) per request."""
     return [[] for _ in range(num_seqs)]

@@ -46,6 +46,18 @@ MUTATIONS = {
     "revival_row_not_advanced": ("out[s0 + j] = packed[r]\n                r += 1",
                                  "out[s0 + j] = packed[r]"),
     "revival_local_row": ("out[s0 + j] = packed[r]", "out[j] = packed[r]"),
+    "round_no_subnormals": ("q = np.maximum(e - p, emin - p + 1)", "q = e - p"),
+    "round_truncates": ("np.ldexp(np.round(np.ldexp(x, -q)), q)", "np.ldexp(np.trunc(np.ldexp(x, -q)), q)"),
+    "round_extra_bit": ("q = np.maximum(e - p, emin - p + 1)", "q = np.maximum(e - p - 1, emin - p)"),
+    "rms_sum_not_mean": ("(rows * rows).sum(axis=1, keepdims=True) / rows.shape[1]",
+                         "(rows * rows).sum(axis=1, keepdims=True)"),
+    "rms_eps_outside_sqrt": ("y = rows / np.sqrt(ms + eps)", "y = rows / (np.sqrt(ms) + eps)"),
+    "rms_gain_dropped": ("y = y * np.asarray(gamma, dtype=np.float64)[None, :]", "y = y"),
+    "compact_rmsnorm_gain_dropped": ("return rms_normalize(h, gamma, eps), p_out, cu_out",
+                                     "return rms_normalize(h, None, eps), p_out, cu_out"),
+    "gather_add_sign": ("return round_to_format(h + d, fmt)", "return round_to_format(h - d, fmt)"),
+    "gather_add_delta_shifted": ("d = np.asarray(delta, dtype=np.float64)[: len(h)]",
+                                 "d = np.asarray(delta, dtype=np.float64)[1: len(h) + 1]"),
 }
 
 

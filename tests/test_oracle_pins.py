@@ -416,12 +416,114 @@ def check_widen_bf16():
     np.testing.assert_array_equal(O.widen_bf16(x.view(torch.int16).numpy()), x.to(torch.float64).numpy())
 
 
+def check_round_to_format():
+    """Rounding to a binary format agrees with library conversions that round
+    once, directly from the wider value: numpy's fp64 -> fp32 and fp64 -> f16
+    casts, and torch's fp32 -> bf16 (on fp32 inputs, so one rounding);
+    hand-worked ties go to the even neighbour."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-150, 130, 20000))
+    x[:6] = [0.0, -0.0, 1.0, -2.5, 2.0 ** -149, 3.4e38]
+    np.testing.assert_array_equal(O.round_to_format(x, "f32"), x.astype(np.float32).astype(np.float64))
+    xh = rng.standard_normal(20000) * np.exp2(rng.integers(-28, 17, 20000))
+    with np.errstate(over="ignore"):
+        np.testing.assert_array_equal(O.round_to_format(xh, "f16"),
+                                      xh.astype(np.float16).astype(np.float64))
+    with np.errstate(over="ignore"):
+        xb = x.astype(np.float32)
+    xb = xb[np.isfinite(xb)]
+    tb = torch.from_numpy(xb).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_to_format(xb.astype(np.float64), "bf16"), tb)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 2.0 ** -134])
+    np.testing.assert_array_equal(O.round_to_format(ties, "bf16"), [1.0, 1 + 2.0 ** -6, -1.0, 0.0])
+    np.testing.assert_array_equal(O.round_to_format(np.array([1 + 2.0 ** -11, 65520.0]), "f16"),
+                                  [1.0, np.inf])
+
+
+def check_rmsnorm():
+    """RMS normalisation: torch.nn.functional.rms_norm in fp64 (library
+    routine) with a gain and eps; a constant row c gives c / sqrt(c^2 + eps)
+    times the gain (closed form); with eps = 0 every output row has mean
+    square exactly 1 and scaling a row by a positive factor leaves it
+    unchanged (invariants)."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((37, 96)) * rng.uniform(0.01, 30, (37, 1))
+    g = rng.standard_normal(96)
+    ref = F.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), eps=1e-5).numpy()
+    np.testing.assert_allclose(O.rms_normalize(x, g, 1e-5), ref, rtol=1e-12, atol=1e-12)
+    c = np.full((2, 8), [[3.0], [-0.5]])
+    np.testing.assert_allclose(O.rms_normalize(c, g[:8], 0.25),
+                               c / np.sqrt(c * c + 0.25) * g[:8], rtol=1e-14)
+    y = O.rms_normalize(x, None, 0.0)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(O.rms_normalize(x * 7.5, None, 0.0), y, rtol=1e-13)
+
+
+def check_compact_rmsnorm():
+    """The fused operand is the normalisation of exactly the kept rows, in
+    order: a hand example (G = 2, one request of 5 tokens, mask 1, 0, 1 keeps
+    rows 0, 1, 4), and with every block kept it equals torch's rms_norm of
+    the whole input (gain included)."""
+    x = np.array([[3.0, 4.0], [1.0, 0.0], [9.0, 9.0], [8.0, 8.0], [0.0, -2.0]])
+    pos = np.array([10, 11, 12, 13, 14], dtype=np.int32)
+    y, p_out, cu_out = O.compact_rmsnorm(np.array([1, 0, 1], dtype=np.uint8), x, pos, [0, 5], 2,
+                                         None, 0.0)
+    r = math.sqrt(12.5)
+    np.testing.assert_allclose(y, [[3 / r, 4 / r], [math.sqrt(2), 0.0], [0.0, -math.sqrt(2)]],
+                               rtol=1e-15)
+    np.testing.assert_array_equal(p_out, [10, 11, 14])
+    np.testing.assert_array_equal(cu_out, [0, 3])
+    rng = np.random.default_rng(14)
+    lengths = [70, 0, 33]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T = int(cu[-1])
+    x = rng.standard_normal((T, 16))
+    g = rng.standard_normal(16)
+    ones = np.ones(int(O.block_offsets(cu, 32)[-1]), dtype=np.uint8)
+    y, _, c2 = O.compact_rmsnorm(ones, x, np.zeros(T, dtype=np.int32), cu, 32, g, 1e-6)
+    ref = F.rms_norm(torch.from_numpy(x), (16,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(c2, cu)
+
+
+def check_gather_add():
+    """Residual sum through the row map: on integer-valued rows (exact in
+    every format) the output is frozen[kept token indices] + delta, the
+    indices taken independently by expanding each request's block mask G
+    times; with every block kept the sum equals torch's own bf16 and f16
+    additions (library routines rounding the exact sum once), and adding the
+    negated kept rows gives exact zeros."""
+    rng = np.random.default_rng(15)
+    lengths = [130, 0, 64, 7]
+    G = 32
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    cub = O.block_offsets(cu, G)
+    T = int(cu[-1])
+    mask = (rng.random(int(cub[-1])) < 0.5).astype(np.uint8)
+    idx = np.concatenate([cu[b] + np.flatnonzero(np.repeat(mask[cub[b]:cub[b + 1]], G)[:L])
+                          for b, L in enumerate(lengths)])
+    fr = rng.integers(-100, 100, (T, 6)).astype(np.float64)
+    de = rng.integers(-100, 100, (T, 6)).astype(np.float64)
+    np.testing.assert_array_equal(O.gather_add(mask, fr, de, cu, G, "bf16"), fr[idx] + de[:len(idx)])
+    np.testing.assert_array_equal(O.gather_add(mask, fr, -fr[idx], cu, G, "f16"),
+                                  np.zeros((len(idx), 6)))
+    ones = np.ones(int(cub[-1]), dtype=np.uint8)
+    for fmt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        a = torch.randn(T, 40, dtype=torch.float64).mul(torch.exp2(torch.randint(-12, 12, (T, 1))))
+        a = a.to(tdt)
+        b = torch.randn(T, 40, dtype=torch.float64).to(tdt)
+        np.testing.assert_array_equal(
+            O.gather_add(ones, a.to(torch.float64).numpy(), b.to(torch.float64).numpy(), cu, G, fmt),
+            (a + b).to(torch.float64).numpy())
+
+
 ALL_CHECKS = [
     check_rows_sum_to_one, check_against_sdpa, check_equal_keys_harmonic, check_hand_example,
     check_gqa_peak, check_head_additivity, check_n1_textbook_softmax, check_block_means,
     check_select_golden, check_one_hot, check_uniform_ceil, check_select_invariants,
     check_brute_force, check_scale_invariance, check_concentration, check_short_requests,
-    check_compaction, check_revival, check_history, check_widen_bf16,
+    check_compaction, check_revival, check_history, check_widen_bf16, check_round_to_format,
+    check_rmsnorm, check_compact_rmsnorm, check_gather_add,
 ]
 
 
