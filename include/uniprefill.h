@@ -15,6 +15,11 @@
  * and, around it,
  *   up_kv_len       per-layer KV length read back from the ledger
  *   up_revive       scatter of packed kept rows back into the full buffer
+ * and, fused:
+ *   up_score_select     up_score + up_select_topp, selection in the epilogue
+ * and, fused into the next layer's first reads (no compacted copy),
+ *   up_compact_rmsnorm  normalised input operand of the kept rows
+ *   up_gather_add       residual sum with the residual read from frozen rows
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -65,6 +70,14 @@ typedef enum up_status {
   UP_ERR_CAPACITY = 4,    /* output capacity smaller than the worst case       */
   UP_ERR_HIP = 5          /* the HIP runtime reported an error                 */
 } up_status;
+
+/* Element type of the entry points that compute on row elements (the
+ * compaction and revival copies move bytes and take no element type). */
+typedef enum up_dtype {
+  UP_DTYPE_BF16 = 0,
+  UP_DTYPE_F16 = 1,
+  UP_DTYPE_F32 = 2
+} up_dtype;
 
 /* ABI version of the loaded library (UP_ABI_VERSION of its build). */
 int up_abi_version(void);
@@ -277,6 +290,95 @@ up_status up_revive(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu
                     const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
                     const void* packed, void* full, int64_t row_bytes, int64_t row_stride_bytes,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Fused pipeline: selection inside the scoring epilogue (§三)               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * up_score_select — up_score followed by up_select_topp in one call, with
+ * the selection run by the scoring epilogue itself: the workgroup that
+ * finishes the last block score of a request selects that request's blocks
+ * (§三: scores, block aggregation and the binary mask without a round trip).
+ * Outputs are bit-identical to up_score then up_select_topp with the same
+ * arguments (the same device code selects on the same block scores).
+ * Arguments: those of up_score, then those of up_select_topp.  The
+ * workspace is up_score's (it holds one arrival counter per request, reset
+ * by every call; calls sharing a workspace run one at a time).  Requests
+ * with no tokens get kept_tokens 0.
+ */
+up_status up_score_select(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                          const int32_t* cu_blocks_d, const void* q, int64_t q_tok_stride,
+                          int64_t q_head_stride, int hq, const void* k, int64_t k_tok_stride,
+                          int64_t k_head_stride, int hkv, int head_dim, int n_query, int block,
+                          float scale, float* token_scores, float* block_scores, double top_p,
+                          int sink, int tail, uint8_t* block_mask, int32_t* kept_tokens,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Fused pipeline: the next layer reads the kept rows itself (§二 step 3)    */
+/* ------------------------------------------------------------------------ */
+/*
+ * Later layers work on the kept tokens only while the dropped ones stay
+ * frozen in place (§二 step 3).  The first reads of the next layer are its
+ * input normalisation and, at its end, the residual that its output is
+ * added to.  These two calls perform those reads straight from the frozen
+ * buffer through the compaction's row map, so no compacted copy of the
+ * hidden states has to be written and read back: the gather costs the kept
+ * rows' read only (the normalised operand and the residual sum are written
+ * by the next layer in any case).  Reading: the next layer is pre-norm with
+ * an RMS normalisation, as in the models the page evaluates.
+ *
+ * Both take the packing arguments of up_compact (block, block_mask, cu_*),
+ * share its workspace (prepared by up_compact_workspace_init, one call at a
+ * time) and run its scan first; rows are `hidden_dim` elements of `dtype`,
+ * a multiple of 16 bytes and at most 16 KiB; every row buffer is 16-byte
+ * aligned and strides are in elements (multiples of 16 bytes); otherwise
+ * UP_ERR_UNSUPPORTED.  Arithmetic is fp32; results are rounded to dtype
+ * (nearest even).  Two launches each: the scan, then one wave per row.
+ */
+
+/*
+ * up_compact_rmsnorm — the next layer's normalised input operand for the
+ * kept tokens, read from the frozen rows:
+ *   normed_out[i] = hidden[t_i] / sqrt(mean_k hidden[t_i][k]^2 + eps) * gamma
+ * where t_i is the i-th kept token (request, then token order), plus the
+ * kept positions and cu_seqlens_out exactly as up_compact writes them.
+ * hidden        [T rows], row t at hidden + t*row_stride (elements).
+ * gamma         [hidden_dim] of dtype, or NULL for a gain of 1.
+ * eps           >= 0 (an all-zero row with eps = 0 gives NaN, as the formula).
+ * normed_out    [out_capacity_rows, hidden_dim] contiguous (written).
+ * residual_out  [out_capacity_rows, hidden_dim] contiguous, or NULL: when set,
+ *               also receives the kept rows unchanged (the compacted copy).
+ * positions, positions_out, cu_seqlens_out, out_capacity_rows  as up_compact.
+ */
+up_status up_compact_rmsnorm(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                             const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                             up_dtype dtype, const void* hidden, int64_t hidden_dim,
+                             int64_t row_stride, const void* gamma, float eps,
+                             const int32_t* positions, void* normed_out, void* residual_out,
+                             int32_t* positions_out, int32_t* cu_seqlens_out,
+                             int64_t out_capacity_rows, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * up_gather_add — the next layer's residual sum for the kept tokens, with
+ * the residual read from the frozen rows:
+ *   out[i] = frozen[t_i] + delta[i]     (i over the kept tokens)
+ * frozen   [T rows], row t at frozen + t*row_stride (elements).
+ * delta    [out_rows, hidden_dim] contiguous, e.g. the layer's output
+ *          projection of the rows up_compact_rmsnorm normalised.
+ * out      [out_rows, hidden_dim] contiguous (written); may be the same
+ *          buffer as delta (in-place residual add), must not overlap frozen.
+ * out_rows should be >= the number of kept tokens (cu_seqlens_out[B] of the
+ *          same mask); a kept block that would end past out_rows is skipped,
+ *          so nothing is read or written beyond out_rows.
+ */
+up_status up_gather_add(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                        const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                        up_dtype dtype, const void* frozen, int64_t hidden_dim, int64_t row_stride,
+                        const void* delta, void* out, int64_t out_rows, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -154,3 +154,40 @@ def oracle_qk(inputs, n_query):
         if ne:
             q64[s1 - ne:s1] = bf16_to_f64(q[s1 - ne:s1])
     return q64, bf16_to_f64(inputs["k"])
+
+
+# Significant bits and smallest normal exponent of the row formats.
+_FMT_BITS = {"bf16": (8, -126), "f16": (11, -14), "f32": (24, -126)}
+FMT_OF = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}
+
+
+def ulp(y: np.ndarray, fmt: str) -> np.ndarray:
+    """Spacing of the format's values at |y| (subnormal spacing below the
+    smallest normal)."""
+    p, emin = _FMT_BITS[fmt]
+    _, e = np.frexp(np.abs(np.asarray(y, dtype=np.float64)))
+    return np.ldexp(1.0, np.maximum(e - p, emin - p + 1))
+
+
+def check_rounded(gpu: np.ndarray, exact: np.ndarray, fmt: str, rel: float, what: str):
+    """A result computed in fp32 and rounded once to fmt: within half an ulp
+    of fmt plus the fp32 arithmetic's relative error `rel` of the exact value.
+    Returns the fraction of elements equal to the correctly rounded value."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert gpu.shape == exact.shape, (gpu.shape, exact.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    tol = 0.5 * ulp(exact, fmt) + rel * np.abs(exact)
+    bad = np.abs(gpu - exact) > tol
+    if bad.any():
+        i = np.unravel_index(int(np.flatnonzero(bad)[0]), bad.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; first at "
+                             f"{i}: gpu {gpu[i]!r} exact {exact[i]!r} tol {tol[i]!r}")
+    return float((gpu == O.round_to_format(exact, fmt)).mean()) if gpu.size else 1.0
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact fp64 values of a bf16 / f16 / f32 tensor."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return bf16_to_f64(t)
+    return t.to(torch.float64).numpy()

@@ -152,3 +152,55 @@ def test_kv_len_rejects_bad_arguments():
     assert lib.up_kv_len(16, 2, 0, 0, 16, 16, None) == 1
     assert lib.up_kv_len(16, 2, 4, 0, None, 16, None) == 1
     assert lib.up_kv_len(16, 0, 4, 0, None, None, None) == 0   # no requests: nothing to do
+
+
+def test_compact_rmsnorm_rejects_bad_arguments():
+    lib = U.lib()
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    # num_seqs, cu_h, cu_d, cu_blocks_d, block, mask, dtype, hidden, hidden_dim, row_stride,
+    # gamma, eps, positions, normed_out, residual_out, positions_out, cu_out, capacity, ws,
+    # ws_bytes, stream
+    base = [1, cu.data_ptr(), 16, 16, 64, 16, 0, 4096, 2048, 2048, None, 1e-6, 16, 8192, None, 16,
+            16, 256, 256, 1 << 20, None]
+    cases = [((17, 255), 4, "capacity"), ((6, 7), 1, "dtype"), ((8, 2049), 2, "multiple of 16"),
+             ((8, 16384), 2, "16 KiB"), ((9, 2047), 2, "row stride"), ((7, 4100), 2, "aligned"),
+             ((11, -1.0), 1, "eps"), ((12, None), 1, "positions"), ((4, 0), 1, "block"),
+             ((19, 16), 3, "workspace"), ((13, None), 1, "NULL"), ((10, 8), 2, "aligned")]
+    for (i, v), status, msg in cases:
+        a = list(base)
+        a[i] = v
+        st = lib.up_compact_rmsnorm(*a)
+        assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())
+
+
+def test_gather_add_rejects_bad_arguments():
+    lib = U.lib()
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    # num_seqs, cu_h, cu_d, cu_blocks_d, block, mask, dtype, frozen, hidden_dim, row_stride,
+    # delta, out, out_rows, ws, ws_bytes, stream
+    base = [1, cu.data_ptr(), 16, 16, 64, 16, 2, 4096, 1024, 1024, 8192, 8192, 256, 256, 1 << 20,
+            None]
+    cases = [((12, -1), 1, "out_rows"), ((6, 3), 1, "dtype"), ((10, None), 1, "NULL"),
+             ((11, 8200), 2, "aligned"), ((9, 1026), 2, "row stride"), ((14, 16), 3, "workspace"),
+             ((8, 0), 1, "hidden_dim")]
+    for (i, v), status, msg in cases:
+        a = list(base)
+        a[i] = v
+        st = lib.up_gather_add(*a)
+        assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())
+
+
+def test_score_select_rejects_bad_arguments():
+    lib = U.lib()
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    # up_score's arguments (workspace last before stream), selection in between
+    base = [1, cu.data_ptr(), 16, 16, 4096, 1024, 128, 8, 8192, 1024, 128, 8, 128, 128, 64, 0.0,
+            None, 16, 0.99, 128, 128, 16, 16, 256, 1 << 30, None]
+    cases = [((18, 0.0), 1, "top_p"), ((18, 1.5), 1, "top_p"), ((19, -1), 1, "sink"),
+             ((22, None), 1, "NULL"), ((21, None), 1, "NULL"), ((12, 96), 2, "head_dim"),
+             ((14, 48), 2, "block"), ((24, 16), 3, "workspace")]
+    for (i, v), status, msg in cases:
+        a = list(base)
+        a[i] = v
+        st = lib.up_score_select(*a)
+        assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())

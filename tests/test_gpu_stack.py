@@ -11,7 +11,7 @@ import torch
 import oracle as O
 import token_block_sparsification_amd as U
 from token_block_sparsification_amd.stack import HybridStack, StackConfig
-from _parity import bf16_to_f64, check_mask, check_scores
+from _parity import bf16_to_f64, check_mask, check_rounded, check_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -25,14 +25,17 @@ def _inputs(cfg, lengths, seed):
     return h, cu, pos
 
 
-@pytest.mark.parametrize("top_p", [0.9, 0.6])
-def test_stack_layers_match_oracle(top_p):
+@pytest.mark.parametrize("top_p,fused", [(0.9, False), (0.6, False), (0.9, True), (0.6, True)])
+def test_stack_layers_match_oracle(top_p, fused):
+    """fused=False compacts at each pruning layer; fused=True reads the kept
+    rows from the frozen buffer for the layer's normalised operand and its
+    residual sum instead (no compacted copy)."""
     cfg = StackConfig(pattern="LFLLFF", d_model=256, d_ff=512, hq=4, hkv=2, head_dim=64,
                       n_query=64, block=32, top_p=top_p, sink=64, tail=64, seed=11)
     stack = HybridStack(cfg, "cuda")
     lengths = [700, 0, 300, 1500, 40]
     h, cu, pos = _inputs(cfg, lengths, 3)
-    res = stack.forward(h, cu, pos, prune=True, keep_records=True)
+    res = stack.forward(h, cu, pos, prune=True, keep_records=True, fused=fused)
     torch.cuda.synchronize()
     assert [r.layer for r in res.records] == cfg.full_layers
     ref_led = O.history_new(len(lengths))
@@ -51,12 +54,21 @@ def test_stack_layers_match_oracle(top_p):
         mask = rec.mask.cpu().numpy()
         check_mask(mask, rec.block_scores.cpu().numpy().astype(np.float64), cu_in, G, cfg.top_p,
                    cfg.sink, cfg.tail)
-        # compaction of this layer's rows and positions, bit for bit
-        h_in = rec.h_in.contiguous().view(torch.int16).cpu().numpy()
         p_in = rec.positions_in.cpu().numpy()
-        h_ref, p_ref, cu_ref = O.compact(mask, h_in, p_in, cu_in, G)
+        if not fused:
+            # compaction of this layer's rows and positions, bit for bit
+            h_in = rec.h_in.contiguous().view(torch.int16).cpu().numpy()
+            h_ref, p_ref, cu_ref = O.compact(mask, h_in, p_in, cu_in, G)
+            assert np.array_equal(rec.h_out.contiguous().view(torch.int16).cpu().numpy(), h_ref)
+        else:
+            # normalised operand read from the frozen rows; residual sum through the row map
+            h64 = bf16_to_f64(rec.h_in)
+            y, p_ref, cu_ref = O.compact_rmsnorm(mask, h64, p_in, cu_in, G, None, 1e-6)
+            check_rounded(bf16_to_f64(rec.normed), y, "bf16", (cfg.d_model / 64 + 16) * 2.0 ** -24,
+                          "normed operand")
+            out_ref = O.gather_add(mask, h64, bf16_to_f64(rec.delta), cu_in, G, "bf16")
+            assert np.array_equal(bf16_to_f64(rec.h_out), out_ref)
         assert list(rec.cu_out.numpy()) == list(cu_ref)
-        assert np.array_equal(rec.h_out.contiguous().view(torch.int16).cpu().numpy(), h_ref)
         assert np.array_equal(rec.positions_out.cpu().numpy(), p_ref)
         O.history_append(ref_led, rec.layer, cu_ref)
         # drops compose: the surviving positions are the earlier survivors,

@@ -24,6 +24,7 @@ __all__ = [
     "up_score_workspace_size", "up_score", "up_select_topp",
     "up_compact_workspace_size", "up_compact_workspace_init", "up_compact",
     "up_history_bytes", "up_history_init", "up_drop_history", "up_kv_len", "up_revive",
+    "up_compact_rmsnorm", "up_gather_add", "up_score_select",
     "Batch", "Workspace", "run_chain",
 ]
 
@@ -58,6 +59,8 @@ _SIGNATURES = {
     "up_score": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I, _P, _I64, _I64, _I, _I, _I, _I, _F,
                       _P, _P, _P, _SZ, _P]),
     "up_select_topp": (_I, [_I, _P, _P, _P, _P, _I, _D, _I, _I, _P, _P, _P]),
+    "up_score_select": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I, _P, _I64, _I64, _I, _I, _I, _I,
+                             _F, _P, _P, _D, _I, _I, _P, _P, _P, _SZ, _P]),
     "up_compact_workspace_size": (_I, [_I, _P, _I, ctypes.POINTER(_SZ)]),
     "up_compact_workspace_init": (_I, [_P, _SZ, _P]),
     "up_compact": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _SZ,
@@ -67,6 +70,10 @@ _SIGNATURES = {
     "up_drop_history": (_I, [_P, _I, _I, _I, _P, _P]),
     "up_kv_len": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "up_revive": (_I, [_I, _P, _P, _P, _I, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "up_compact_rmsnorm": (_I, [_I, _P, _P, _P, _I, _P, _I, _P, _I64, _I64, _P, _F, _P, _P, _P,
+                                _P, _P, _I64, _P, _SZ, _P]),
+    "up_gather_add": (_I, [_I, _P, _P, _P, _I, _P, _I, _P, _I64, _I64, _P, _P, _I64, _P, _SZ,
+                           _P]),
 }
 
 
@@ -185,6 +192,25 @@ def up_score(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, q, k, n_query: int, block:
     _check("up_score", st)
 
 
+def up_score_select(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, q, k, n_query: int, block: int,
+                    scale: float, token_scores: Optional[torch.Tensor], block_scores: torch.Tensor,
+                    top_p: float, sink: int, tail: int, block_mask, kept_tokens,
+                    workspace: torch.Tensor, stream=None) -> None:
+    """up_score and up_select_topp in one call, the selection run by the
+    scoring epilogue (fused pipeline); same outputs as the two calls."""
+    _bf16_3d("q", q)
+    _bf16_3d("k", k)
+    cu = _host_i32(cu_seqlens_h)
+    st = lib().up_score_select(
+        cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_d), _ptr(cu_blocks_d),
+        _ptr(q), q.stride(0), q.stride(1), q.shape[1],
+        _ptr(k), k.stride(0), k.stride(1), k.shape[1],
+        q.shape[2], n_query, block, float(scale),
+        _ptr(token_scores), _ptr(block_scores), float(top_p), sink, tail, _ptr(block_mask),
+        _ptr(kept_tokens), _ptr(workspace), workspace.numel(), _stream(stream, q.device))
+    _check("up_score_select", st)
+
+
 def up_select_topp(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block_scores, block: int,
                    top_p: float, sink: int, tail: int, block_mask, kept_tokens,
                    stream=None) -> None:
@@ -254,6 +280,51 @@ def up_revive(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, p
                          _ptr(block_mask), _ptr(packed), _ptr(full), row_bytes, row_stride,
                          _ptr(workspace), workspace.numel(), _stream(stream, full.device))
     _check("up_revive", st)
+
+
+_DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+
+
+def _rows_2d(name, t):
+    if t.dtype not in _DTYPES or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a bf16/f16/f32 [rows, D] tensor with a contiguous last dim")
+
+
+def up_compact_rmsnorm(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, hidden,
+                       gamma: Optional[torch.Tensor], eps: float, positions, normed_out,
+                       residual_out: Optional[torch.Tensor], positions_out, cu_seqlens_out,
+                       workspace, stream=None) -> None:
+    """The next layer's RMS-normalised operand of the kept rows, read straight
+    from the frozen rows (§二 step 3, fused pipeline): hidden [T, D]."""
+    _rows_2d("hidden", hidden)
+    for n, t in (("normed_out", normed_out), ("residual_out", residual_out), ("gamma", gamma)):
+        if t is not None and (t.dtype != hidden.dtype or not t.is_contiguous()):
+            raise ValueError(f"{n} must be contiguous with hidden's dtype")
+    cu = _host_i32(cu_seqlens_h)
+    st = lib().up_compact_rmsnorm(cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_d), _ptr(cu_blocks_d),
+                                  block, _ptr(block_mask), _DTYPES[hidden.dtype], _ptr(hidden),
+                                  hidden.shape[1], hidden.stride(0), _ptr(gamma), eps,
+                                  _ptr(positions), _ptr(normed_out), _ptr(residual_out),
+                                  _ptr(positions_out), _ptr(cu_seqlens_out), normed_out.shape[0],
+                                  _ptr(workspace), workspace.numel(),
+                                  _stream(stream, normed_out.device))
+    _check("up_compact_rmsnorm", st)
+
+
+def up_gather_add(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, frozen, delta,
+                  out, workspace, stream=None) -> None:
+    """Residual sum of the kept rows with the residual read from the frozen
+    rows: out[i] = frozen[i-th kept token] + delta[i] (fused pipeline)."""
+    _rows_2d("frozen", frozen)
+    for n, t in (("delta", delta), ("out", out)):
+        if t.dtype != frozen.dtype or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{n} must be a contiguous [rows, D] tensor with frozen's dtype")
+    cu = _host_i32(cu_seqlens_h)
+    st = lib().up_gather_add(cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_d), _ptr(cu_blocks_d), block,
+                             _ptr(block_mask), _DTYPES[frozen.dtype], _ptr(frozen), frozen.shape[1],
+                             frozen.stride(0), _ptr(delta), _ptr(out), out.shape[0],
+                             _ptr(workspace), workspace.numel(), _stream(stream, out.device))
+    _check("up_gather_add", st)
 
 
 # ---------------------------------------------------------------------------

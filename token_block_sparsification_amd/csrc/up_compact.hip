@@ -27,6 +27,10 @@
 // Splitting the gather from the scan lets the copy use small, uniform work
 // items (the shape a plain device copy runs fastest with) instead of one
 // workgroup per scan tile.
+#include <math.h>
+
+#include <initializer_list>
+
 #include "up_internal.h"
 
 namespace up {
@@ -331,6 +335,197 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_copy_kernel(Compac
 }
 
 // ---------------------------------------------------------------------------
+// Fused pipeline: the next layer reads the kept rows through the copy
+// descriptors instead of a compacted copy.
+//   NORM  out[dst + i] = RMSNorm(frozen[src + i]) * gamma   (the next layer's
+//         normalised input operand; optionally also the residual copy)
+//   ADD   out[dst + i] = frozen[src + i] + delta[dst + i]   (the next layer's
+//         residual sum, with the residual gathered from the frozen rows)
+// One wave per row: a row of up to 16 KiB is held in registers as 16-byte
+// vectors (VPL per lane), its sum of squares reduced over the wave in a fixed
+// butterfly order (bitwise reproducible), then scaled and rounded to the
+// element type.  A work item is (block, group of 4*U rows), U rows per wave in
+// flight, so each item moves tens of KiB like the plain copy's pieces.
+// ---------------------------------------------------------------------------
+enum { kDtBf16 = 0, kDtF16 = 1, kDtF32 = 2 };
+enum { kOpNorm = 0, kOpAdd = 1 };
+
+struct RowOpArgs {
+  const BlockCopy* desc;
+  int64_t num_blocks;
+  int pieces;          // work items per block
+  int rows_per_item;   // 4 waves * U
+  const char* src;     // frozen rows (input), src_stride bytes apart
+  int64_t src_stride;
+  const char* delta;   // ADD: [kept rows] delta_stride bytes apart
+  int64_t delta_stride;
+  char* out;           // [kept rows] out_stride bytes apart
+  int64_t out_stride;
+  char* res_out;       // NORM: residual copy or NULL
+  int64_t res_stride;
+  const char* gamma;   // NORM: gain [D] or NULL
+  const int32_t* positions;
+  int32_t* positions_out;
+  int64_t nvec;        // 16-byte vectors per row
+  float inv_d, eps;
+};
+
+template <int DT> struct Elem;
+template <> struct Elem<kDtBf16> {
+  static constexpr int PER = 8;  // elements per 16-byte vector
+  static __device__ __forceinline__ void unpack(u32x4_t v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  // fp32 -> bf16, round to nearest even (finite values; NaN stays NaN)
+  static __device__ __forceinline__ uint32_t round1(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  }
+  static __device__ __forceinline__ u32x4_t pack(const float (&f)[8]) {
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = round1(f[2 * i]) | (round1(f[2 * i + 1]) << 16);
+    return v;
+  }
+};
+template <> struct Elem<kDtF16> {
+  static constexpr int PER = 8;
+  static __device__ __forceinline__ void unpack(u32x4_t v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i] & 0xffffu));
+      f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i] >> 16));
+    }
+  }
+  static __device__ __forceinline__ u32x4_t pack(const float (&f)[8]) {
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)f[2 * i]);
+      const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)f[2 * i + 1]);
+      v[i] = lo | (hi << 16);
+    }
+    return v;
+  }
+};
+template <> struct Elem<kDtF32> {
+  static constexpr int PER = 4;
+  static __device__ __forceinline__ void unpack(u32x4_t v, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+  static __device__ __forceinline__ u32x4_t pack(const float (&f)[4]) {
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+    return v;
+  }
+};
+
+template <int OP, int DT, int VPL, int U>
+__global__ void __launch_bounds__(kCompactThreads) up_rowop_kernel(RowOpArgs a) {
+  using E = Elem<DT>;
+  constexpr int PER = E::PER;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t items = a.num_blocks * a.pieces;
+  for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+    const int64_t b = w / a.pieces;
+    const int piece = (int)(w - b * a.pieces);
+    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(a.desc + b);
+    const int64_t dst = (int64_t)(((uint64_t)raw[1] << 32) | raw[0]);
+    const int32_t src = (int32_t)raw[2];
+    const int32_t rows = (int32_t)raw[3];
+    if (dst < 0) continue;  // dropped block (uniform over the workgroup)
+    if (OP == kOpNorm && a.positions && piece == 0)
+      for (int i = threadIdx.x; i < rows; i += kCompactThreads)
+        a.positions_out[dst + i] = a.positions[src + i];
+    const int r0 = piece * a.rows_per_item + wave * U;
+    u32x4_t x[U][VPL], y[U][VPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u;
+      if (r >= rows) continue;
+      const u32x4_t* s = reinterpret_cast<const u32x4_t*>(a.src + (int64_t)(src + r) * a.src_stride);
+      const u32x4_t* d =
+          reinterpret_cast<const u32x4_t*>(a.delta + (int64_t)(dst + r) * a.delta_stride);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int64_t c = lane + 64 * v;
+        if (c < a.nvec) {
+          x[u][v] = __builtin_nontemporal_load(s + c);
+          if (OP == kOpAdd) y[u][v] = __builtin_nontemporal_load(d + c);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u;
+      if (r >= rows) continue;
+      u32x4_t* o = reinterpret_cast<u32x4_t*>(a.out + (int64_t)(dst + r) * a.out_stride);
+      if (OP == kOpAdd) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          const int64_t c = lane + 64 * v;
+          if (c < a.nvec) {
+            float f[PER], g[PER];
+            E::unpack(x[u][v], f);
+            E::unpack(y[u][v], g);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) f[e] += g[e];
+            __builtin_nontemporal_store(E::pack(f), o + c);
+          }
+        }
+      } else {
+        float ss = 0.f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          if (lane + 64 * v < a.nvec) {
+            float f[PER];
+            E::unpack(x[u][v], f);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) ss = fmaf(f[e], f[e], ss);
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        const float rs = rsqrtf(ss * a.inv_d + a.eps);
+        // Unpack the row again below instead of keeping every element live
+        // as fp32 across the reduction (that would double the registers).
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) __asm__ volatile("" : "+v"(x[u][v]));
+        u32x4_t* ro = a.res_out
+                          ? reinterpret_cast<u32x4_t*>(a.res_out + (int64_t)(dst + r) * a.res_stride)
+                          : nullptr;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          const int64_t c = lane + 64 * v;
+          if (c < a.nvec) {
+            float f[PER];
+            E::unpack(x[u][v], f);
+            if (a.gamma) {
+              float g[PER];
+              E::unpack(reinterpret_cast<const u32x4_t*>(a.gamma)[c], g);
+#pragma unroll
+              for (int e = 0; e < PER; ++e) f[e] = f[e] * rs * g[e];
+            } else {
+#pragma unroll
+              for (int e = 0; e < PER; ++e) f[e] = f[e] * rs;
+            }
+            __builtin_nontemporal_store(E::pack(f), o + c);
+            if (ro) __builtin_nontemporal_store(x[u][v], ro + c);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Drop-history ledger.
 // ---------------------------------------------------------------------------
 constexpr int kLedgerHeader = 4;
@@ -467,7 +662,11 @@ void launch_copy(const up::CompactArgs& a, dim3 grid, uintptr_t al, hipStream_t 
                        stream, a);
 }
 
-up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
+// Validates a gather call, fills the kernel arguments and enqueues the scan
+// (descriptors, and cu_seqlens_out when c.cu_out is set).  *ran is false when
+// there is nothing to do (no requests).
+up_status scan_for(const GatherCall& c, int64_t T, up::CompactArgs* out, bool* ran) {
+  *ran = false;
   if (c.block < 1 || c.block > 4096) return up::set_error(UP_ERR_INVALID, "block not in [1, 4096]");
   if (c.row_bytes < 1 || c.row_stride < c.row_bytes)
     return up::set_error(UP_ERR_INVALID, "need row_bytes >= 1 and row_stride_bytes >= row_bytes");
@@ -483,7 +682,8 @@ up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
   up_status st = up::check_device();
   if (st != UP_OK) return st;
 
-  up::CompactArgs a{};
+  up::CompactArgs& a = *out;
+  a = up::CompactArgs{};
   a.cu_seqlens = c.cu_d;
   a.cu_blocks = c.cu_blocks_d;
   a.mask = c.mask;
@@ -502,6 +702,18 @@ up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
   a.block = c.block;
   a.num_blocks = lay.blocks;
   a.num_tiles = lay.tiles;
+  hipLaunchKernelGGL(up::up_compact_scan_kernel, dim3((unsigned)(a.num_tiles > 0 ? a.num_tiles : 1)),
+                     dim3(up::kCompactThreads), 0, c.stream, a);
+  st = up::check_launch("up_compact_scan_kernel");
+  *ran = st == UP_OK;
+  return st;
+}
+
+up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
+  up::CompactArgs a;
+  bool ran;
+  up_status st = scan_for(c, T, &a, &ran);
+  if (st != UP_OK || !ran || a.num_blocks == 0) return st;
   if (c.row_stride == c.row_bytes) {
     // kPieceBytes pieces, larger (4 KiB multiples) if a block would need more
     // than 65535 of them (keeps the item count of huge rows bounded)
@@ -517,12 +729,6 @@ up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
     if (a.piece_rows > c.block) a.piece_rows = c.block;
     a.pieces = up::ceil_div(c.block, a.piece_rows);
   }
-
-  hipLaunchKernelGGL(up::up_compact_scan_kernel, dim3((unsigned)(a.num_tiles > 0 ? a.num_tiles : 1)),
-                     dim3(up::kCompactThreads), 0, c.stream, a);
-  st = up::check_launch("up_compact_scan_kernel");
-  if (st != UP_OK || a.num_blocks == 0) return st;
-
   const int64_t items = a.num_blocks * a.pieces;
   const dim3 grid((unsigned)(items < (int64_t)1 << 30 ? items : (int64_t)1 << 30));
   const uintptr_t al = (uintptr_t)c.hidden | (uintptr_t)c.hidden_out | (uintptr_t)c.row_bytes |
@@ -530,6 +736,62 @@ up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
   if (revive) launch_copy<true>(a, grid, al, c.stream);
   else launch_copy<false>(a, grid, al, c.stream);
   return up::check_launch("up_compact_copy_kernel");
+}
+
+// ---------------------------------------------------------------------------
+// Fused row operations (host side).
+// ---------------------------------------------------------------------------
+int elem_bytes(up_dtype dt) { return dt == UP_DTYPE_F32 ? 4 : 2; }
+
+template <int OP, int DT, int VPL>
+void launch_rowop_vpl(up::RowOpArgs a, int64_t num_blocks, int block, hipStream_t st) {
+  constexpr int U = VPL >= 8 ? 1 : VPL >= 2 ? 8 / VPL : 4;  // rows per wave in flight
+  a.rows_per_item = 4 * U;
+  a.pieces = (int)up::ceil_div(block, a.rows_per_item);
+  const int64_t items = num_blocks * a.pieces;
+  const dim3 grid((unsigned)(items < (int64_t)1 << 30 ? items : (int64_t)1 << 30));
+  hipLaunchKernelGGL((up::up_rowop_kernel<OP, DT, VPL, U>), grid, dim3(up::kCompactThreads), 0, st, a);
+}
+
+template <int OP, int DT>
+void launch_rowop_dt(const up::RowOpArgs& a, int64_t num_blocks, int block, hipStream_t st) {
+  const int64_t vpl = up::ceil_div(a.nvec, 64);
+  if (vpl <= 1) launch_rowop_vpl<OP, DT, 1>(a, num_blocks, block, st);
+  else if (vpl <= 2) launch_rowop_vpl<OP, DT, 2>(a, num_blocks, block, st);
+  else if (vpl <= 4) launch_rowop_vpl<OP, DT, 4>(a, num_blocks, block, st);
+  else if (vpl <= 8) launch_rowop_vpl<OP, DT, 8>(a, num_blocks, block, st);
+  else launch_rowop_vpl<OP, DT, 16>(a, num_blocks, block, st);
+}
+
+template <int OP>
+void launch_rowop(up_dtype dt, const up::RowOpArgs& a, int64_t num_blocks, int block, hipStream_t st) {
+  switch (dt) {
+    case UP_DTYPE_BF16: launch_rowop_dt<OP, up::kDtBf16>(a, num_blocks, block, st); break;
+    case UP_DTYPE_F16: launch_rowop_dt<OP, up::kDtF16>(a, num_blocks, block, st); break;
+    default: launch_rowop_dt<OP, up::kDtF32>(a, num_blocks, block, st); break;
+  }
+}
+
+// Checks shared by the fused row operations: element type, row geometry in
+// 16-byte vectors (at most 16 KiB per row), 16-byte alignment of every row.
+up_status check_rows(up_dtype dt, int64_t hidden_dim, std::initializer_list<int64_t> strides,
+                     std::initializer_list<const void*> ptrs) {
+  if (dt != UP_DTYPE_BF16 && dt != UP_DTYPE_F16 && dt != UP_DTYPE_F32)
+    return up::set_error(UP_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (hidden_dim < 1) return up::set_error(UP_ERR_INVALID, "hidden_dim < 1");
+  const int64_t rb = hidden_dim * elem_bytes(dt);
+  if (rb % 16 != 0 || rb > 16384)
+    return up::set_error(UP_ERR_UNSUPPORTED,
+                         "rows of %lld bytes: need a multiple of 16 bytes, at most 16 KiB",
+                         (long long)rb);
+  for (int64_t s : strides)
+    if (s < hidden_dim || (s * elem_bytes(dt)) % 16 != 0)
+      return up::set_error(UP_ERR_UNSUPPORTED,
+                           "row stride %lld: need >= hidden_dim and a multiple of 16 bytes",
+                           (long long)s);
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return up::set_error(UP_ERR_UNSUPPORTED, "row buffers must be 16-byte aligned");
+  return UP_OK;
 }
 
 }  // namespace
@@ -603,6 +865,96 @@ up_status up_revive(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu
                row_bytes, row_stride_bytes, nullptr, const_cast<void*>(packed), nullptr, nullptr,
                T, workspace, workspace_bytes, stream};
   return run_gather(c, T, true);
+}
+
+up_status up_compact_rmsnorm(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                             const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                             up_dtype dtype, const void* hidden, int64_t hidden_dim,
+                             int64_t row_stride, const void* gamma, float eps,
+                             const int32_t* positions, void* normed_out, void* residual_out,
+                             int32_t* positions_out, int32_t* cu_seqlens_out,
+                             int64_t out_capacity_rows, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  up::clear_error();
+  int64_t T;
+  int max_len;
+  up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &max_len);
+  if (st != UP_OK) return st;
+  if (out_capacity_rows < T)
+    return up::set_error(UP_ERR_CAPACITY, "out_capacity_rows %lld < T %lld",
+                         (long long)out_capacity_rows, (long long)T);
+  if (!cu_seqlens_out || (T > 0 && (!hidden || !normed_out)))
+    return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if ((positions == nullptr) != (positions_out == nullptr))
+    return up::set_error(UP_ERR_INVALID, "positions and positions_out must both be set or both NULL");
+  if (!(eps >= 0.f) || !isfinite(eps)) return up::set_error(UP_ERR_INVALID, "eps must be finite and >= 0");
+  st = check_rows(dtype, hidden_dim, {row_stride, hidden_dim},
+                  {hidden, normed_out, residual_out, gamma});
+  if (st != UP_OK) return st;
+  const int64_t eb = elem_bytes(dtype);
+  GatherCall c{num_seqs,  cu_seqlens_h, cu_seqlens_d,  cu_blocks_d,    block,
+               block_mask, hidden,      hidden_dim * eb, row_stride * eb, positions,
+               normed_out, positions_out, cu_seqlens_out, out_capacity_rows,
+               workspace,  workspace_bytes, stream};
+  up::CompactArgs ca;
+  bool ran;
+  st = scan_for(c, T, &ca, &ran);
+  if (st != UP_OK || !ran || ca.num_blocks == 0) return st;
+  up::RowOpArgs a{};
+  a.desc = ca.desc;
+  a.num_blocks = ca.num_blocks;
+  a.src = static_cast<const char*>(hidden);
+  a.src_stride = row_stride * eb;
+  a.out = static_cast<char*>(normed_out);
+  a.out_stride = hidden_dim * eb;
+  a.res_out = static_cast<char*>(residual_out);
+  a.res_stride = hidden_dim * eb;
+  a.gamma = static_cast<const char*>(gamma);
+  a.positions = positions;
+  a.positions_out = positions_out;
+  a.nvec = hidden_dim * eb / 16;
+  a.inv_d = 1.0f / (float)hidden_dim;
+  a.eps = eps;
+  launch_rowop<up::kOpNorm>(dtype, a, ca.num_blocks, block, stream);
+  return up::check_launch("up_rowop_kernel");
+}
+
+up_status up_gather_add(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                        const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                        up_dtype dtype, const void* frozen, int64_t hidden_dim, int64_t row_stride,
+                        const void* delta, void* out, int64_t out_rows, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  up::clear_error();
+  int64_t T;
+  int max_len;
+  up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &max_len);
+  if (st != UP_OK) return st;
+  if (out_rows < 0) return up::set_error(UP_ERR_INVALID, "out_rows < 0");
+  if (T > 0 && out_rows > 0 && (!frozen || !delta || !out))
+    return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  st = check_rows(dtype, hidden_dim, {row_stride, hidden_dim}, {frozen, delta, out});
+  if (st != UP_OK) return st;
+  const int64_t eb = elem_bytes(dtype);
+  GatherCall c{num_seqs, cu_seqlens_h, cu_seqlens_d,    cu_blocks_d,     block,
+               block_mask, frozen,     hidden_dim * eb, row_stride * eb, nullptr,
+               out,      nullptr,      nullptr,         out_rows,
+               workspace, workspace_bytes, stream};
+  up::CompactArgs ca;
+  bool ran;
+  st = scan_for(c, T, &ca, &ran);
+  if (st != UP_OK || !ran || ca.num_blocks == 0) return st;
+  up::RowOpArgs a{};
+  a.desc = ca.desc;
+  a.num_blocks = ca.num_blocks;
+  a.src = static_cast<const char*>(frozen);
+  a.src_stride = row_stride * eb;
+  a.delta = static_cast<const char*>(delta);
+  a.delta_stride = hidden_dim * eb;
+  a.out = static_cast<char*>(out);
+  a.out_stride = hidden_dim * eb;
+  a.nvec = hidden_dim * eb / 16;
+  launch_rowop<up::kOpAdd>(dtype, a, ca.num_blocks, block, stream);
+  return up::check_launch("up_rowop_kernel");
 }
 
 up_status up_kv_len(void* ledger, int num_seqs, int capacity, int layer_id,

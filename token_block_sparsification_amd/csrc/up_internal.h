@@ -34,7 +34,7 @@ struct ScoreGeometry {
   int rg_a;          // row-statistics row groups per KV head
   int ck;            // keys per workgroup chunk
   int max_chunks;    // chunks of the longest request
-  size_t off_partial, off_bias, off_colpart, bytes;
+  size_t off_partial, off_bias, off_colpart, off_arrive, bytes;
 };
 
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv,

@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "up_internal.h"
+#include "up_select_impl.h"
 
 namespace up {
 namespace {
@@ -57,7 +58,14 @@ struct ScoreArgs {
   float* token_scores;
   float* block_scores;
   int64_t num_blocks;
+  uint32_t* arrive;  // [B] workgroups of each request done in the epilogue
+  int32_t* kept;     // fused selection: kept tokens [B] (requests without blocks get 0 here)
 };
+
+__global__ void up_zero_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -511,6 +519,13 @@ up_rowstats_kernel(ScoreArgs a) {
 // per row, lanes over chunks, fixed-order butterfly reductions.
 __global__ void __launch_bounds__(256) up_rowstats_combine_kernel(ScoreArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The epilogue's per-request arrival counters start every call at zero.
+  if (blockIdx.x == 0)
+    for (int r = threadIdx.x; r < a.num_seqs; r += 256) {
+      a.arrive[r] = 0;
+      // a request without blocks never reaches the epilogue's selection
+      if (a.kept && a.cu_blocks[r + 1] == a.cu_blocks[r]) a.kept[r] = 0;
+    }
   const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
   const int64_t total = (int64_t)a.num_seqs * a.hq * a.n_query;
   if (idx >= total) return;
@@ -755,37 +770,75 @@ up_colsum_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 // Epilogue: token score = fixed-order sum of the per-(KV head, row group)
 // partials; block score = mean over the block's tokens.  One wave per block.
+// SELECT (fused pipeline): each workgroup then counts its blocks into their
+// requests' arrival counters; the workgroup that completes a request runs
+// that request's Top-p selection (select_request) on the block scores, so
+// no separate selection launch is needed.  Every wave fences its block score
+// (device scope) before the count, and the selecting workgroup fences
+// before reading, so it sees every block score of the request whichever XCD
+// wrote it.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
+template <bool SELECT>
+__global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a, SelectArgs sa) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * 4 + wave;
-  if (b >= a.num_blocks) return;
-  // request owning block b: last r with cu_blocks[r] <= b
-  int lo = 0, hi = a.num_seqs;  // invariant: cu_blocks[lo] <= b < cu_blocks[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
-  }
-  const int r = lo;
-  const int s0 = a.cu_seqlens[r];
-  const int L = a.cu_seqlens[r + 1] - s0;
-  const int lb = (int)(b - a.cu_blocks[r]);
-  const int j0 = lb * a.block, j1 = min(j0 + a.block, L);
-  // only the row groups that hold rows of this request wrote partials
-  const int n_eff = min(a.n_query, L);
-  const int rg_used = (a.rgqa * n_eff + a.rows_per_wg - 1) / a.rows_per_wg;
-  float sum = 0.f;
-  for (int j = j0 + lane; j < j1; j += 64) {
-    float c = 0.f;
-    for (int g = 0; g < a.hkv; ++g)
-      for (int rgi = 0; rgi < rg_used; ++rgi)
-        c += a.colpart[((int64_t)g * a.rg + rgi) * a.T + s0 + j];
-    if (a.token_scores) a.token_scores[s0 + j] = c;
-    sum += c;
-  }
+  const bool valid = b < a.num_blocks;
+  int r = -1;
+  if (valid) {
+    // request owning block b: last r with cu_blocks[r] <= b
+    int lo = 0, hi = a.num_seqs;  // invariant: cu_blocks[lo] <= b < cu_blocks[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
+    }
+    r = lo;
+    const int s0 = a.cu_seqlens[r];
+    const int L = a.cu_seqlens[r + 1] - s0;
+    const int lb = (int)(b - a.cu_blocks[r]);
+    const int j0 = lb * a.block, j1 = min(j0 + a.block, L);
+    // only the row groups that hold rows of this request wrote partials
+    const int n_eff = min(a.n_query, L);
+    const int rg_used = (a.rgqa * n_eff + a.rows_per_wg - 1) / a.rows_per_wg;
+    float sum = 0.f;
+    for (int j = j0 + lane; j < j1; j += 64) {
+      float c = 0.f;
+      for (int g = 0; g < a.hkv; ++g)
+        for (int rgi = 0; rgi < rg_used; ++rgi)
+          c += a.colpart[((int64_t)g * a.rg + rgi) * a.T + s0 + j];
+      if (a.token_scores) a.token_scores[s0 + j] = c;
+      sum += c;
+    }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-  if (lane == 0) a.block_scores[b] = sum / (float)(j1 - j0);
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) a.block_scores[b] = sum / (float)(j1 - j0);
+  }
+  if constexpr (SELECT) {
+    __shared__ SelectShared sh;
+    __shared__ int s_req[4];
+    __shared__ int s_sel[4];
+    __shared__ int s_nsel;
+    __threadfence();  // this wave's block score is visible device-wide
+    if (lane == 0) s_req[wave] = r;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int n = 0;
+      for (int w = 0; w < 4; ++w) {
+        const int rq = s_req[w];
+        if (rq < 0 || (w > 0 && s_req[w - 1] == rq)) continue;
+        uint32_t c = 1;
+        while (w + (int)c < 4 && s_req[w + c] == rq) ++c;  // blocks are ordered by request
+        const uint32_t nb = (uint32_t)(a.cu_blocks[rq + 1] - a.cu_blocks[rq]);
+        const uint32_t prev = __hip_atomic_fetch_add(&a.arrive[rq], c, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + c == nb) s_sel[n++] = rq;
+      }
+      s_nsel = n;
+    }
+    __syncthreads();
+    const int nsel = s_nsel;
+    if (nsel > 0) __threadfence();  // acquire: the other workgroups' block scores
+    for (int i = 0; i < nsel; ++i) select_request(sa, s_sel[i], sh);
+  }
 }
 
 // Compile-time tiling per head_dim and pass: NT 32-row tiles per wave, W
@@ -924,6 +977,8 @@ up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int h
   off = up::align_up(off + (size_t)num_seqs * hq * n_query * sizeof(float), 256);
   g.off_colpart = off;
   off = up::align_up(off + (size_t)hkv * g.rg * (size_t)T * sizeof(float), 256);
+  g.off_arrive = off;
+  off = up::align_up(off + (size_t)num_seqs * sizeof(uint32_t), 256);
   g.bytes = off > 0 ? off : 256;
   out->g = g;
   out->bytes = g.bytes;
@@ -945,13 +1000,24 @@ up_status up_score_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int
   return UP_OK;
 }
 
-up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
-                   const int32_t* cu_blocks_d, const void* q, int64_t q_tok_stride,
-                   int64_t q_head_stride, int hq, const void* k, int64_t k_tok_stride,
-                   int64_t k_head_stride, int hkv, int head_dim, int n_query, int block, float scale,
-                   float* token_scores, float* block_scores, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
-  up::clear_error();
+}  // extern "C"
+
+namespace {
+
+// Selection arguments of the fused entry point (NULL for up_score).
+struct SelectParams {
+  double top_p;
+  int sink, tail;
+  uint8_t* block_mask;
+  int32_t* kept_tokens;
+};
+
+up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                     const int32_t* cu_blocks_d, const void* q, int64_t q_tok_stride,
+                     int64_t q_head_stride, int hq, const void* k, int64_t k_tok_stride,
+                     int64_t k_head_stride, int hkv, int head_dim, int n_query, int block,
+                     float scale, float* token_scores, float* block_scores, void* workspace,
+                     size_t workspace_bytes, const SelectParams* sel, hipStream_t stream) {
   Layout lay;
   up_status st = score_layout(num_seqs, cu_seqlens_h, hq, hkv, head_dim, n_query, &lay);
   if (st != UP_OK) return st;
@@ -962,7 +1028,25 @@ up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_
   const int64_t T = cu_seqlens_h[num_seqs];
   int64_t N = 0;
   for (int r = 0; r < num_seqs; ++r) N += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], block);
-  if (num_seqs == 0 || T == 0) return UP_OK;  // nothing to score
+  if (sel) {
+    if (!(sel->top_p > 0.0 && sel->top_p <= 1.0))
+      return up::set_error(UP_ERR_INVALID, "top_p not in (0, 1]");
+    if (sel->sink < 0 || sel->tail < 0)
+      return up::set_error(UP_ERR_INVALID, "sink and tail must be >= 0");
+    if (num_seqs > 0 && (!sel->kept_tokens || !cu_seqlens_d || !cu_blocks_d))
+      return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+    if (T > 0 && !sel->block_mask) return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  }
+  if (num_seqs == 0) return UP_OK;
+  if (T == 0) {
+    // nothing to score; every request keeps 0 tokens
+    if (!sel) return UP_OK;
+    st = up::check_device();
+    if (st != UP_OK) return st;
+    hipLaunchKernelGGL(up::up_zero_kernel, dim3((unsigned)up::ceil_div(num_seqs, 256)), dim3(256), 0,
+                       stream, sel->kept_tokens, num_seqs);
+    return up::check_launch("up_zero_kernel");
+  }
   if (!cu_seqlens_d || !cu_blocks_d || !q || !k || !block_scores || !workspace)
     return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
   if (((uintptr_t)q & 15) || ((uintptr_t)k & 15) || (q_tok_stride & 7) || (q_head_stride & 7) ||
@@ -1010,6 +1094,8 @@ up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_
   a.token_scores = token_scores;
   a.block_scores = block_scores;
   a.num_blocks = N;
+  a.arrive = reinterpret_cast<uint32_t*>(ws + lay.g.off_arrive);
+  a.kept = sel ? sel->kept_tokens : nullptr;
 
   a.num_groups = 0;
   for (int r = 0; r < num_seqs; ++r)
@@ -1023,11 +1109,50 @@ up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_
   }
   if (st != UP_OK) return st;
   if (N > 0) {
-    hipLaunchKernelGGL(up::up_blockmean_kernel, dim3((unsigned)up::ceil_div(N, 4)), dim3(256), 0,
-                       stream, a);
+    up::SelectArgs sa{};
+    if (sel) {
+      sa = up::SelectArgs{cu_seqlens_d, cu_blocks_d, block_scores, sel->block_mask,
+                          sel->kept_tokens, block, sel->sink, sel->tail, sel->top_p};
+      hipLaunchKernelGGL(up::up_blockmean_kernel<true>, dim3((unsigned)up::ceil_div(N, 4)),
+                         dim3(256), 0, stream, a, sa);
+    } else {
+      hipLaunchKernelGGL(up::up_blockmean_kernel<false>, dim3((unsigned)up::ceil_div(N, 4)),
+                         dim3(256), 0, stream, a, sa);
+    }
     st = up::check_launch("up_blockmean_kernel");
   }
   return st;
 }
+
+}  // namespace
+
+extern "C" {
+
+up_status up_score(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                   const int32_t* cu_blocks_d, const void* q, int64_t q_tok_stride,
+                   int64_t q_head_stride, int hq, const void* k, int64_t k_tok_stride,
+                   int64_t k_head_stride, int hkv, int head_dim, int n_query, int block, float scale,
+                   float* token_scores, float* block_scores, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  up::clear_error();
+  return score_call(num_seqs, cu_seqlens_h, cu_seqlens_d, cu_blocks_d, q, q_tok_stride,
+                    q_head_stride, hq, k, k_tok_stride, k_head_stride, hkv, head_dim, n_query, block,
+                    scale, token_scores, block_scores, workspace, workspace_bytes, nullptr, stream);
+}
+
+up_status up_score_select(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                          const int32_t* cu_blocks_d, const void* q, int64_t q_tok_stride,
+                          int64_t q_head_stride, int hq, const void* k, int64_t k_tok_stride,
+                          int64_t k_head_stride, int hkv, int head_dim, int n_query, int block,
+                          float scale, float* token_scores, float* block_scores, double top_p,
+                          int sink, int tail, uint8_t* block_mask, int32_t* kept_tokens,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  up::clear_error();
+  const SelectParams sel{top_p, sink, tail, block_mask, kept_tokens};
+  return score_call(num_seqs, cu_seqlens_h, cu_seqlens_d, cu_blocks_d, q, q_tok_stride,
+                    q_head_stride, hq, k, k_tok_stride, k_head_stride, hkv, head_dim, n_query, block,
+                    scale, token_scores, block_scores, workspace, workspace_bytes, &sel, stream);
+}
+
 
 }  // extern "C"

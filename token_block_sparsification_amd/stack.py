@@ -21,6 +21,12 @@ Weights are seeded random bf16 (there is no trained model); the F layers'
 attention output itself is not computed, since it is not part of the pruning
 path.  Every step of the pruning path runs in the library's kernels; the
 projections and MLPs are plain torch matrix products (contiguous operands).
+
+fused=True runs the fused pipeline at each F layer: no compacted copy of the
+hidden states is made; the layer's normalised operand is read straight from
+the frozen rows (up_compact_rmsnorm) and its residual sum reads the residual
+from them too (up_gather_add).  fused=False compacts first (up_compact) and
+normalises / adds with torch.
 """
 from __future__ import annotations
 
@@ -29,8 +35,9 @@ from typing import List, Optional
 
 import torch
 
-from . import (Batch, up_compact, up_drop_history, up_history_bytes, up_history_init,
-               up_score, up_score_workspace_size, up_select_topp, new_compact_workspace)
+from . import (Batch, up_compact, up_compact_rmsnorm, up_drop_history, up_gather_add,
+               up_history_bytes, up_history_init, up_score, up_score_workspace_size,
+               up_select_topp, new_compact_workspace)
 
 
 @dataclass
@@ -70,6 +77,8 @@ class LayerRecord:
     cu_out: Optional[torch.Tensor] = None
     h_out: Optional[torch.Tensor] = None
     positions_out: Optional[torch.Tensor] = None
+    normed: Optional[torch.Tensor] = None   # fused: the normalised operand of the kept rows
+    delta: Optional[torch.Tensor] = None    # fused: the output projection added to the residual
 
 
 @dataclass
@@ -113,9 +122,10 @@ class HybridStack:
                 raise ValueError(f"unknown layer kind {kind!r}")
 
     def forward(self, hidden: torch.Tensor, cu_seqlens, positions: torch.Tensor,
-                prune: bool = True, keep_records: bool = False) -> StackResult:
+                prune: bool = True, keep_records: bool = False, fused: bool = False) -> StackResult:
         """Run the stack on a packed batch.  prune=False carries every token
-        through (the same layers, no pruning path) for comparison."""
+        through (the same layers, no pruning path) for comparison; fused=True
+        uses the fused pipeline at the pruning layers."""
         cfg = self.cfg
         cu = torch.as_tensor(cu_seqlens, dtype=torch.int32).cpu()
         h, pos = hidden, positions
@@ -147,6 +157,13 @@ class HybridStack:
             # in either mode; the pruning path only reuses them.
             q = (x @ wts["wq"]).view(T, cfg.hq, cfg.head_dim)
             k = (x @ wts["wk"]).view(T, cfg.hkv, cfg.head_dim)
+            if prune and T > 0 and fused:
+                h, pos, cu_new, rec = self._prune_fused(li, h, pos, cu, q, k, ledger, nf,
+                                                        keep_records, wts["wo"])
+                if rec is not None:
+                    res.records.append(rec)
+                cu = cu_new
+                continue
             if prune and T > 0:
                 h, pos, cu_new, rec = self._prune(li, h, pos, cu, q, k, ledger, nf, keep_records)
                 if rec is not None:
@@ -158,7 +175,8 @@ class HybridStack:
         res.hidden, res.positions, res.cu_seqlens = h, pos, cu
         return res
 
-    def _prune(self, li, h, pos, cu, q, k, ledger, nf, keep_records):
+    def _select(self, cu, q, k):
+        """Scores and mask of one full-attention layer (library kernels)."""
         cfg = self.cfg
         dev = self.dev
         batch = Batch.make(cu, cfg.block, dev)
@@ -176,6 +194,43 @@ class HybridStack:
                  sws)
         up_select_topp(cu, batch.cu_seqlens_d, batch.cu_blocks_d, bs, cfg.block, cfg.top_p, cfg.sink,
                        cfg.tail, mask, kept)
+        return batch, ts, bs, mask
+
+    def _prune_fused(self, li, h, pos, cu, q, k, ledger, nf, keep_records, wo):
+        """Fused pipeline at a pruning layer: the normalised operand and the
+        residual sum read the kept rows from the frozen buffer `h` through
+        the row map; no compacted copy of `h` is written."""
+        cfg = self.cfg
+        dev = self.dev
+        batch, ts, bs, mask = self._select(cu, q, k)
+        T, N, B = batch.num_tokens, batch.num_blocks, batch.num_seqs
+        cws = self._ws[1]
+        x = torch.empty_like(h)
+        p_out = torch.empty_like(pos)
+        cu_out = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        up_compact_rmsnorm(cu, batch.cu_seqlens_d, batch.cu_blocks_d, cfg.block, mask, h, None,
+                           1e-6, pos, x, None, p_out, cu_out, cws)
+        up_drop_history(ledger, B, nf, li, cu_out)
+        cu_new = cu_out.cpu()  # the following layers size their launches on the host
+        n = int(cu_new[-1])
+        delta = x[:n] @ wo
+        delta_in = delta.clone() if keep_records else None
+        up_gather_add(cu, batch.cu_seqlens_d, batch.cu_blocks_d, cfg.block, mask, h, delta, delta,
+                      cws)  # in place: delta becomes the layer's output rows
+        rec = None
+        if keep_records:
+            rec = LayerRecord(layer=li, cu_in=cu, tokens_in=T, tokens_out=n, q=q, k=k, h_in=h,
+                              positions_in=pos, token_scores=ts, block_scores=bs[:N],
+                              mask=mask[:N], cu_out=cu_new, h_out=delta, positions_out=p_out[:n],
+                              normed=x[:n], delta=delta_in)
+        return delta, p_out[:n], cu_new, rec
+
+    def _prune(self, li, h, pos, cu, q, k, ledger, nf, keep_records):
+        cfg = self.cfg
+        dev = self.dev
+        batch, ts, bs, mask = self._select(cu, q, k)
+        T, N, B = batch.num_tokens, batch.num_blocks, batch.num_seqs
+        cws = self._ws[1]
         h_out = torch.empty_like(h)
         p_out = torch.empty_like(pos)
         cu_out = torch.empty(B + 1, dtype=torch.int32, device=dev)
