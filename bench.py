@@ -86,6 +86,8 @@ TRAFFIC_KERNELS = {
     "up_rowstats_kernel": ("up_score.hip", r"\bup_rowstats_kernel\b"),
     "up_colsum_kernel": ("up_score.hip", r"\bup_colsum_kernel\b"),
     "up_select_kernel": ("up_select.hip", r"\bup_select_kernel\b"),
+    "up_rowop_kernel_norm": ("up_compact.hip", r"\bup_rowop_kernel<0, "),
+    "up_rowop_kernel_add": ("up_compact.hip", r"\bup_rowop_kernel<1, "),
 }
 
 
@@ -274,6 +276,42 @@ def main():
         rv_marks.append(m)
     torch.cuda.synchronize()
 
+    # Fused pipeline, outside the timed region: selection in the scoring
+    # epilogue, and the next layer's normalised operand / residual sum read
+    # straight from the frozen rows, against the unfused calls (compaction,
+    # then torch's RMSNorm of the compacted rows).
+    D = hidden.shape[1]
+    normed = torch.empty((T, D), dtype=hidden.dtype, device=dev)
+    delta = torch.randn((max(kept, 1), D), device=dev).to(hidden.dtype)
+    fz = []
+    for i in range(nb):
+        m = new_marks(["up_score_select", "up_compact_rmsnorm", "up_gather_add", "torch_rmsnorm",
+                       "chain_fused"])
+        m["chain_fused"][0].record()
+        m["up_score_select"][0].record()
+        U.up_score_select(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, q, k,
+                          w.n_query, w.block, 0.0, ws.token_scores, ws.block_scores, w.top_p,
+                          w.sink, w.tail, ws.block_mask, ws.kept_tokens, ws.score_ws)
+        m["up_score_select"][1].record()
+        m["up_compact_rmsnorm"][0].record()
+        U.up_compact_rmsnorm(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, w.block,
+                             ws.block_mask, hidden, None, 1e-6, pos, normed, None, ws.positions_out,
+                             ws.cu_seqlens_out, ws.compact_ws)
+        m["up_compact_rmsnorm"][1].record()
+        U.up_drop_history(ledger, B, cap, (K + i) % cap, ws.cu_seqlens_out)
+        m["chain_fused"][1].record()
+        m["up_gather_add"][0].record()
+        U.up_gather_add(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, w.block,
+                        ws.block_mask, hidden, delta, normed[:max(kept, 1)], ws.compact_ws)
+        m["up_gather_add"][1].record()
+        m["torch_rmsnorm"][0].record()
+        torch.nn.functional.rms_norm(ws.hidden_out[:kept], (D,), eps=1e-6)
+        m["torch_rmsnorm"][1].record()
+        fz.append(m)
+    torch.cuda.synchronize()
+    U.up_history_init(ledger, B, cap)
+    del normed, delta
+
     ms_per_step = (t1 - t0) * 1e3 / K
     per_call_us = {n: mean_us(brk, n) for n in calls}
     per_call_us[dominant] = dominant_us
@@ -317,6 +355,37 @@ def main():
                     "unit": "TFLOP/s", "frac": round(score_tflops_exec / PEAK_BF16_TFLOPS, 4),
                     "traffic": None, "algorithmic_flops_per_launch": flops_exec}
 
+    # fused pipeline figures
+    fz_us = {n: mean_us(fz, n) for n in fz[0]}
+    norm_bytes = 2 * kept * row_bytes + 2 * 4 * kept + N     # kept rows read, operand written
+    add_bytes = 3 * kept * row_bytes + N                      # frozen + delta read, sum written
+    unfused_chain_us = sum(per_call_us[n] for n in calls) + fz_us["torch_rmsnorm"]
+
+    def gbs(b, us):
+        return round(b / (us * 1e-6) / 1e9, 1)
+
+    fused_rec = {
+        "up_score_select_us": round(fz_us["up_score_select"], 2),
+        "up_score_plus_select_us": round(per_call_us["up_score"] + per_call_us["up_select_topp"], 2),
+        "up_compact_rmsnorm_us": round(fz_us["up_compact_rmsnorm"], 2),
+        "up_compact_rmsnorm_gbs": gbs(norm_bytes, fz_us["up_compact_rmsnorm"]),
+        "up_compact_rmsnorm_frac_of_hbm_peak": round(gbs(norm_bytes, fz_us["up_compact_rmsnorm"]) / PEAK_HBM_GBS, 4),
+        "up_compact_rmsnorm_algorithmic_bytes": int(norm_bytes),
+        "up_compact_rmsnorm_traffic": (lambda a, b: a + b if a is not None and b is not None else None)(
+            load_traffic("up_rowop_kernel_norm", "up_compact.hip"),
+            load_traffic("up_compact_scan_kernel", "up_compact.hip")),
+        "up_gather_add_us": round(fz_us["up_gather_add"], 2),
+        "up_gather_add_gbs": gbs(add_bytes, fz_us["up_gather_add"]),
+        "up_gather_add_frac_of_hbm_peak": round(gbs(add_bytes, fz_us["up_gather_add"]) / PEAK_HBM_GBS, 4),
+        "up_gather_add_algorithmic_bytes": int(add_bytes),
+        "unfused_compact_then_torch_rmsnorm_us": round(per_call_us["up_compact"] + fz_us["torch_rmsnorm"], 2),
+        "chain_fused_us": round(fz_us["chain_fused"], 2),
+        "chain_unfused_with_torch_rmsnorm_us": round(unfused_chain_us, 2),
+        "note": ("chain_fused = up_score_select + up_compact_rmsnorm + up_drop_history (the "
+                 "next layer's normalised operand produced from the frozen rows); the unfused "
+                 "chain adds torch's RMSNorm of the compacted rows to the four calls"),
+    }
+
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -353,6 +422,7 @@ def main():
                        load_traffic("up_revive_copy_kernel", "up_compact.hip"),
                        load_traffic("up_compact_scan_kernel", "up_compact.hip"))},
         "kv_len_us": round(mean_us(rv_marks, "up_kv_len"), 2),
+        "fused_pipeline": fused_rec,
         "keep_ratio": round(kept / T, 5),
         "input_generation_s": round(t_gen, 2),
     }
@@ -377,14 +447,14 @@ def stack_bench(args, dev):
     cu = torch.tensor([0, L], dtype=torch.int32)
     pos = torch.arange(L, dtype=torch.int32, device=dev)
 
-    def timed(stack, prune, reps=5):
+    def timed(stack, prune, reps=5, fused=False):
         for _ in range(2):
-            stack.forward(h, cu, pos, prune=prune)
+            stack.forward(h, cu, pos, prune=prune, fused=fused)
         torch.cuda.synchronize()
         times = []
         for _ in range(reps):
             t0 = time.perf_counter()
-            r = stack.forward(h, cu, pos, prune=prune)
+            r = stack.forward(h, cu, pos, prune=prune, fused=fused)
             torch.cuda.synchronize()
             times.append(time.perf_counter() - t0)
         return float(np.median(times)), r
@@ -398,7 +468,10 @@ def stack_bench(args, dev):
         if t_full is None:
             t_full, _ = timed(stack, False)
         t, r = timed(stack, True)
+        tf, rf = timed(stack, True, fused=True)
         runs.append({"top_p": p, "ms": round(t * 1e3, 3), "speedup_vs_unpruned": round(t_full / t, 4),
+                     "fused_ms": round(tf * 1e3, 3), "fused_speedup_vs_unpruned": round(t_full / tf, 4),
+                     "fused_tokens_per_layer": rf.tokens_per_layer,
                      "tokens_per_layer": r.tokens_per_layer,
                      "layer_tokens_fraction": round(sum(r.tokens_per_layer) /
                                                     (L * len(cfg.pattern)), 4)})

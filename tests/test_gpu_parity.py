@@ -183,7 +183,8 @@ def test_select_isolated():
     within the fixed-point resolution of p * total)."""
     dev = torch.device("cuda")
     G = 16
-    lens = [0, 5, 16 * 100000, 16 * 3000 - 7, 16 * 1000, 16 * 40, 16 * 40, 16 * 40]
+    lens = [0, 5, 16 * 100000, 16 * 3000 - 7, 16 * 1000, 16 * 40, 16 * 40, 16 * 40,
+            16 * 2000, 16 * 2000, 16 * 4096, 16 * 4097]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     batch = U.Batch.make(torch.from_numpy(cu), G, dev)
     cub = batch.cu_blocks_h.numpy()
@@ -193,6 +194,17 @@ def test_select_isolated():
     sc[cub[6]:cub[7]] = 0.0
     sc[cub[6] + 17] = 3.0
     sc[cub[7]:cub[8]] = 0.0
+    # request 8: few distinct values (ties at every level); 9: scores spread
+    # over 2^-20 .. 2^20 (keys differ in the exponent: every radix digit
+    # used; every mass stays far above the fixed-point resolution); 10 / 11:
+    # near-uniform scores at the LDS staging limit and one block past it
+    n8 = cub[9] - cub[8]
+    sc[cub[8]:cub[9]] = (np.arange(n8) * 7919 % 5 + 1).astype(np.float32) * 0.25
+    n9 = cub[10] - cub[9]
+    sc[cub[9]:cub[10]] = np.exp2(np.linspace(-20, 20, n9) * ((np.arange(n9) * 31 % 17) / 16.0))
+    for r in (10, 11):
+        n = cub[r + 1] - cub[r]
+        sc[cub[r]:cub[r + 1]] = (1.0 + 1e-3 * W.gen.make_scores(80 + r, n).numpy()).astype(np.float32)
     for p, sink, tail in [(0.99, 128, 128), (0.5, 0, 16), (1.0, 32, 32), (0.9, 0, 0)]:
         bs = torch.from_numpy(sc).to(dev)
         mask = torch.empty(batch.num_blocks, dtype=torch.uint8, device=dev)

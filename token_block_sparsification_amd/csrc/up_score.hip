@@ -778,67 +778,102 @@ up_colsum_kernel(ScoreArgs a) {
 // before reading, so it sees every block score of the request whichever XCD
 // wrote it.
 // ---------------------------------------------------------------------------
-template <bool SELECT>
-__global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a, SelectArgs sa) {
+// One wave per block score; writes it unless `score` is given (then the
+// caller stores it).
+__device__ __forceinline__ int blockmean_one(const ScoreArgs& a, int64_t b, int lane,
+                                             float* score = nullptr) {
+  // request owning block b: last r with cu_blocks[r] <= b
+  int lo = 0, hi = a.num_seqs;  // invariant: cu_blocks[lo] <= b < cu_blocks[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
+  }
+  const int r = lo;
+  const int s0 = a.cu_seqlens[r];
+  const int L = a.cu_seqlens[r + 1] - s0;
+  const int lb = (int)(b - a.cu_blocks[r]);
+  const int j0 = lb * a.block, j1 = min(j0 + a.block, L);
+  // only the row groups that hold rows of this request wrote partials
+  const int n_eff = min(a.n_query, L);
+  const int rg_used = (a.rgqa * n_eff + a.rows_per_wg - 1) / a.rows_per_wg;
+  float sum = 0.f;
+  for (int j = j0 + lane; j < j1; j += 64) {
+    float c = 0.f;
+    for (int g = 0; g < a.hkv; ++g)
+      for (int rgi = 0; rgi < rg_used; ++rgi)
+        c += a.colpart[((int64_t)g * a.rg + rgi) * a.T + s0 + j];
+    if (a.token_scores) a.token_scores[s0 + j] = c;
+    sum += c;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (score) *score = sum / (float)(j1 - j0);
+  else if (lane == 0) a.block_scores[b] = sum / (float)(j1 - j0);
+  return r;
+}
+
+// Blocks per workgroup of the selecting epilogue (UP_SEL_BPW / 4 per wave).
+#ifndef UP_SEL_BPW
+#define UP_SEL_BPW 4
+#endif
+constexpr int kSelBlocksPerWg = UP_SEL_BPW;
+
+__global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * 4 + wave;
-  const bool valid = b < a.num_blocks;
-  int r = -1;
-  if (valid) {
-    // request owning block b: last r with cu_blocks[r] <= b
-    int lo = 0, hi = a.num_seqs;  // invariant: cu_blocks[lo] <= b < cu_blocks[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
-    }
-    r = lo;
-    const int s0 = a.cu_seqlens[r];
-    const int L = a.cu_seqlens[r + 1] - s0;
-    const int lb = (int)(b - a.cu_blocks[r]);
-    const int j0 = lb * a.block, j1 = min(j0 + a.block, L);
-    // only the row groups that hold rows of this request wrote partials
-    const int n_eff = min(a.n_query, L);
-    const int rg_used = (a.rgqa * n_eff + a.rows_per_wg - 1) / a.rows_per_wg;
-    float sum = 0.f;
-    for (int j = j0 + lane; j < j1; j += 64) {
-      float c = 0.f;
-      for (int g = 0; g < a.hkv; ++g)
-        for (int rgi = 0; rgi < rg_used; ++rgi)
-          c += a.colpart[((int64_t)g * a.rg + rgi) * a.T + s0 + j];
-      if (a.token_scores) a.token_scores[s0 + j] = c;
-      sum += c;
-    }
+  if (b < a.num_blocks) blockmean_one(a, b, lane);
+}
+
+// Fused selection: each workgroup computes kSelBlocksPerWg block scores (its
+// four waves share them out) into LDS; wave 0 stores them, releases them at
+// device scope
+// (its own stores, one fence per workgroup) and adds the workgroup's blocks
+// to each touched request's arrival counter.  The workgroup that completes a
+// request acquires at device scope and runs that request's Top-p selection
+// (select_request) on the block scores, whichever XCD wrote them.
+__global__ void __launch_bounds__(256) up_blockmean_select_kernel(ScoreArgs a, SelectArgs sa) {
+  __shared__ SelectShared sh;
+  __shared__ int s_req[kSelBlocksPerWg];
+  __shared__ float s_score[kSelBlocksPerWg];
+  __shared__ int s_sel[kSelBlocksPerWg];
+  __shared__ int s_nsel;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b0 = (int64_t)blockIdx.x * kSelBlocksPerWg;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    if (lane == 0) a.block_scores[b] = sum / (float)(j1 - j0);
+  for (int i = 0; i < kSelBlocksPerWg / 4; ++i) {
+    const int slot = wave * (kSelBlocksPerWg / 4) + i;
+    float sc = 0.f;
+    const int r = b0 + slot < a.num_blocks ? blockmean_one(a, b0 + slot, lane, &sc) : -1;
+    if (lane == 0) {
+      s_req[slot] = r;
+      s_score[slot] = sc;
+    }
   }
-  if constexpr (SELECT) {
-    __shared__ SelectShared sh;
-    __shared__ int s_req[4];
-    __shared__ int s_sel[4];
-    __shared__ int s_nsel;
-    __threadfence();  // this wave's block score is visible device-wide
-    if (lane == 0) s_req[wave] = r;
-    __syncthreads();
-    if (threadIdx.x == 0) {
+  __syncthreads();
+  if (wave == 0) {
+    if (lane < kSelBlocksPerWg && s_req[lane] >= 0) a.block_scores[b0 + lane] = s_score[lane];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // wave 0's stores, visible device-wide
+    if (lane == 0) {
       int n = 0;
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < kSelBlocksPerWg; ++w) {
         const int rq = s_req[w];
         if (rq < 0 || (w > 0 && s_req[w - 1] == rq)) continue;
         uint32_t c = 1;
-        while (w + (int)c < 4 && s_req[w + c] == rq) ++c;  // blocks are ordered by request
+        while (w + (int)c < kSelBlocksPerWg && s_req[w + c] == rq) ++c;  // ordered by request
         const uint32_t nb = (uint32_t)(a.cu_blocks[rq + 1] - a.cu_blocks[rq]);
-        const uint32_t prev = __hip_atomic_fetch_add(&a.arrive[rq], c, __ATOMIC_ACQ_REL,
+        const uint32_t prev = __hip_atomic_fetch_add(&a.arrive[rq], c, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         if (prev + c == nb) s_sel[n++] = rq;
       }
+      if (n > 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       s_nsel = n;
     }
-    __syncthreads();
-    const int nsel = s_nsel;
-    if (nsel > 0) __threadfence();  // acquire: the other workgroups' block scores
-    for (int i = 0; i < nsel; ++i) select_request(sa, s_sel[i], sh);
   }
+  __syncthreads();
+  const int nsel = s_nsel;
+  if (nsel == 0) return;  // uniform
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int i = 0; i < nsel; ++i) select_request(sa, s_sel[i], sh);
 }
 
 // Compile-time tiling per head_dim and pass: NT 32-row tiles per wave, W
@@ -1109,17 +1144,18 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   }
   if (st != UP_OK) return st;
   if (N > 0) {
-    up::SelectArgs sa{};
     if (sel) {
-      sa = up::SelectArgs{cu_seqlens_d, cu_blocks_d, block_scores, sel->block_mask,
-                          sel->kept_tokens, block, sel->sink, sel->tail, sel->top_p};
-      hipLaunchKernelGGL(up::up_blockmean_kernel<true>, dim3((unsigned)up::ceil_div(N, 4)),
-                         dim3(256), 0, stream, a, sa);
+      const up::SelectArgs sa{cu_seqlens_d, cu_blocks_d, block_scores, sel->block_mask,
+                              sel->kept_tokens, block, sel->sink, sel->tail, sel->top_p};
+      hipLaunchKernelGGL(up::up_blockmean_select_kernel,
+                         dim3((unsigned)up::ceil_div(N, up::kSelBlocksPerWg)), dim3(256), 0, stream,
+                         a, sa);
+      st = up::check_launch("up_blockmean_select_kernel");
     } else {
-      hipLaunchKernelGGL(up::up_blockmean_kernel<false>, dim3((unsigned)up::ceil_div(N, 4)),
-                         dim3(256), 0, stream, a, sa);
+      hipLaunchKernelGGL(up::up_blockmean_kernel, dim3((unsigned)up::ceil_div(N, 4)), dim3(256), 0,
+                         stream, a);
+      st = up::check_launch("up_blockmean_kernel");
     }
-    st = up::check_launch("up_blockmean_kernel");
   }
   return st;
 }

@@ -16,13 +16,22 @@
 //      so every sum below is exact and independent of summation order: the
 //      result is bitwise deterministic.
 //   2. R = ceil(p * total) - forced mass is the optional mass still needed.
-//   3. Radix select, most significant 8-bit digit first, over the 32-bit
-//      order-preserving key of each optional block's score: an LDS histogram
-//      of (count, mass) per digit, then one wave scans the 256 buckets from
-//      the top and finds the bucket where the mass from above reaches R.
-//      Four passes give the exact cutoff score v* and the mass above it.
+//   3. Radix select, most significant digit first, over the 32-bit
+//      order-preserving key of each optional block's score.  The bits that
+//      the smallest and the largest optional key share are common to every
+//      optional key, so the digits start at their highest differing bit
+//      (near-uniform scores differ only in low mantissa bits).  Per digit of
+//      8 bits: an LDS histogram of (count, mass), then one wave scans
+//      the buckets from the top and finds the bucket where the mass from
+//      above reaches R.  One to four passes give the exact cutoff score v*
+//      and the mass above it.  The histograms alternate between two LDS
+//      buffers, so clearing the next one overlaps building the current one.
 //   4. Blocks with score v* are tied; the lowest-index ones are kept until the
-//      mass reaches R (a block-wide prefix count over index order).
+//      mass reaches R: each thread takes a contiguous run of blocks, and one
+//      block-wide exclusive scan of the runs' tie counts ranks every tie.
+// A request with at most kStageMax blocks has its keys and fixed-point masses
+// computed once into LDS (every later pass reads them there); longer requests
+// recompute them from the scores in memory on every pass.
 // Fixed point differs from exact fp64 sums by < N * 2^-S of the top score, so
 // a decision can differ from an fp64 evaluation only when the cumulative
 // mass is within that distance of p * total.
@@ -38,6 +47,18 @@ namespace {
 constexpr int kSelectThreads = 256;
 constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int64_t kMaxBlocksPerRequest = 1 << 24;
+constexpr int kStageMax = 4096;         // blocks staged in LDS
+#ifndef UP_SEL_DIGIT_BITS
+#define UP_SEL_DIGIT_BITS 8
+#endif
+constexpr int kDigitBits = UP_SEL_DIGIT_BITS;
+constexpr int kBuckets = 1 << kDigitBits;
+constexpr int kBucketsPerLane = kBuckets / 64;
+// Histogram slot of bucket d: one pad slot per kBucketsPerLane buckets, so the
+// wave that scans the buckets (lane l reads kBucketsPerLane consecutive ones
+// from the top) spreads each step's reads over the LDS banks.
+constexpr int kBucketSlots = kBuckets + kBuckets / kBucketsPerLane;
+__device__ __forceinline__ int bslot(int d) { return d + d / kBucketsPerLane; }
 
 struct SelectArgs {
   const int32_t* cu_seqlens;
@@ -65,6 +86,23 @@ __device__ __forceinline__ uint64_t mass_of(float s, double scale) {
   return m > 0.0 ? (uint64_t)m : 0ull;
 }
 
+struct SelectShared {
+  uint32_t skey[kStageMax];   // staged: order-preserving key (0 for forced blocks)
+  uint64_t smass[kStageMax];  // staged: fixed-point mass
+  uint32_t cnt[2][kBucketSlots];
+  uint64_t mass[2][kBucketSlots];
+  uint64_t red64[2][kSelectWaves];
+  float redf[kSelectWaves];
+  uint32_t redu[2][kSelectWaves];
+  int redi[kSelectWaves];
+  // decision state (written by wave 0, read by all after a barrier)
+  uint32_t prefix;       // known high bits of the cutoff key
+  uint64_t above;        // optional mass with key above the current bucket range
+  int all_optional;      // the optional mass never reaches R: keep every block
+  uint64_t tie_mass;     // mass of one block at the cutoff key
+  uint64_t tie_keep;     // how many tied blocks (lowest index first) are kept
+};
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
@@ -72,53 +110,20 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
-struct SelectShared {
-  uint32_t cnt[256];
-  uint64_t mass[256];
-  uint64_t red[kSelectWaves];
-  float redf[kSelectWaves];
-  int redi[kSelectWaves];
-  // decision state (written by wave 0, read by all after a barrier)
-  uint32_t prefix;       // known high digits of the cutoff key
-  uint64_t above;        // optional mass with key above the current bucket range
-  int64_t need;          // R: optional mass still needed (<= 0: none)
-  int all_optional;      // the optional mass never reaches R: keep every block
-  uint64_t tie_mass;     // mass of one block at the cutoff key
-  uint64_t tie_keep;     // how many tied blocks (lowest index first) are kept
-};
-
-// Block-wide reductions (fixed order: wave butterfly, then waves in order).
-__device__ uint64_t block_sum_u64(uint64_t v, SelectShared& sh) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint64_t s = 0;
-  for (int w = 0; w < kSelectWaves; ++w) s += sh.red[w];
-  return s;
-}
-
-__device__ float block_max(float v, SelectShared& sh) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.redf[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float m = sh.redf[0];
-  for (int w = 1; w < kSelectWaves; ++w) m = fmaxf(m, sh.redf[w]);
-  return m;
-}
-
-// Wave 0: scan buckets 255..0 (descending keys) for the first bucket where
-// above + (mass of this and higher buckets) >= need; refine the state.
-__device__ void pick_bucket(SelectShared& sh, int shift) {
+// Wave 0: scan the buckets from the top (descending keys) for the first
+// bucket where above + (mass of this and higher buckets) >= need; refine the
+// state.  Bucket d of this pass holds keys whose bits [shift, shift + width)
+// equal d (higher bits equal the known prefix).
+__device__ void pick_bucket(SelectShared& sh, int buf, int shift, int width, uint64_t need) {
   const int lane = threadIdx.x & 63;
-  // lane l owns buckets 255-4l .. 252-4l, highest first
-  uint64_t m[4];
+  const int nbk = 1 << width;
+  // lane l owns buckets top-kBucketsPerLane*l ... (highest first)
+  uint64_t m[kBucketsPerLane];
   uint64_t local = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = sh.mass[255 - 4 * lane - i];
+  for (int i = 0; i < kBucketsPerLane; ++i) {
+    const int d = nbk - 1 - kBucketsPerLane * lane - i;
+    m[i] = d >= 0 ? sh.mass[buf][bslot(d)] : 0;
     local += m[i];
   }
   uint64_t incl = local;
@@ -128,7 +133,6 @@ __device__ void pick_bucket(SelectShared& sh, int shift) {
     if (lane >= off) incl += y;
   }
   const uint64_t before = sh.above + (incl - local);  // mass of buckets above this lane's first
-  const uint64_t need = (uint64_t)sh.need;
   const bool crosses = before + local >= need;
   const uint64_t ballot = __ballot(crosses);
   if (ballot == 0) {  // the candidates never reach R (only possible on the first pass)
@@ -139,15 +143,15 @@ __device__ void pick_bucket(SelectShared& sh, int shift) {
   if (lane == first) {
     uint64_t acc = before;
     int i = 0;
-    for (; i < 3; ++i) {
+    for (; i < kBucketsPerLane - 1; ++i) {
       if (acc + m[i] >= need) break;
       acc += m[i];
     }
-    const uint32_t digit = (uint32_t)(255 - 4 * lane - i);
+    const uint32_t digit = (uint32_t)(nbk - 1 - kBucketsPerLane * lane - i);
     sh.prefix |= digit << shift;
     sh.above = acc;
     if (shift == 0) {
-      const uint32_t c = sh.cnt[digit];
+      const uint32_t c = sh.cnt[buf][bslot(digit)];
       sh.tie_mass = c ? m[i] / c : 0;
       const uint64_t rest = need - acc;  // > 0, <= m[i]
       sh.tie_keep = sh.tie_mass ? (rest + sh.tie_mass - 1) / sh.tie_mass : c;
@@ -156,112 +160,189 @@ __device__ void pick_bucket(SelectShared& sh, int shift) {
 }
 
 // Selection of one request by the whole (kSelectThreads-thread) workgroup.
-// Uniform over the workgroup; every thread must call it.
-__device__ void select_request(const SelectArgs& a, int req, SelectShared& sh) {
+// STAGED: the request has at most kStageMax blocks; their keys and masses
+// are computed once into LDS and every later pass reads them from there.
+template <bool STAGED>
+__device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s0 = a.cu_seqlens[req];
   const int L = a.cu_seqlens[req + 1] - s0;
   const int cb0 = a.cu_blocks[req];
-  const int nb = a.cu_blocks[req + 1] - cb0;
-  if (nb <= 0) {
-    if (tid == 0) a.kept[req] = 0;
-    return;
-  }
-  __syncthreads();  // the shared state may still be read by a previous call
   const int G = a.block;
   const float* sc = a.scores + cb0;
 
-  // 1. fixed-point scale from the request's largest score
+  // 1. largest score, smallest / largest optional key (staging the scores)
   float mx = 0.f;
-  for (int i = tid; i < nb; i += kSelectThreads) mx = fmaxf(mx, sc[i]);
-  mx = block_max(mx, sh);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i = tid; i < nb; i += kSelectThreads) {
+    const float s = sc[i];
+    if (STAGED) sh.skey[i] = __float_as_uint(s);
+    mx = fmaxf(mx, s);
+    if (!is_forced(i, L, G, a.sink, a.tail)) {
+      const uint32_t k = orderable(s);
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+  }
+  if (lane == 0) {
+    sh.redf[wave] = mx;
+    sh.redu[0][wave] = kmin;
+    sh.redu[1][wave] = kmax;
+  }
+  __syncthreads();
+  mx = sh.redf[0];
+  kmin = sh.redu[0][0];
+  kmax = sh.redu[1][0];
+  for (int w = 1; w < kSelectWaves; ++w) {
+    mx = fmaxf(mx, sh.redf[w]);
+    kmin = min(kmin, sh.redu[0][w]);
+    kmax = max(kmax, sh.redu[1][w]);
+  }
   int lg = 0;
   while ((1ll << lg) < (int64_t)nb + 1) ++lg;
   const int S = 62 - lg;
   const double scale = mx > 0.f ? ldexp(1.0, S) / (double)mx : 0.0;
 
-  // 2. total and forced mass
+  // Key of an optional block (forced: false) and its mass.
+  auto key_mass = [&](int i, uint32_t& key, uint64_t& m) -> bool {
+    if (STAGED) {
+      key = sh.skey[i];
+      if (key == 0) return false;  // forced
+      m = sh.smass[i];
+      return true;
+    }
+    if (is_forced(i, L, G, a.sink, a.tail)) return false;
+    const float s = sc[i];
+    key = orderable(s);
+    m = mass_of(s, scale);
+    return true;
+  };
+
+  // 2. total and forced mass (one two-value reduction); staged: keys and
+  //    masses into LDS (each thread rewrites the entries it staged)
   uint64_t tot = 0, forced = 0;
   for (int i = tid; i < nb; i += kSelectThreads) {
-    const uint64_t m = mass_of(sc[i], scale);
+    const float s = STAGED ? __uint_as_float(sh.skey[i]) : sc[i];
+    const uint64_t m = mass_of(s, scale);
+    const bool f = is_forced(i, L, G, a.sink, a.tail);
     tot += m;
-    if (is_forced(i, L, G, a.sink, a.tail)) forced += m;
+    if (f) forced += m;
+    if (STAGED) {
+      sh.smass[i] = m;
+      sh.skey[i] = f ? 0u : orderable(s);  // real scores never map to key 0
+    }
   }
-  tot = block_sum_u64(tot, sh);
-  forced = block_sum_u64(forced, sh);
+  tot = wave_sum(tot);
+  forced = wave_sum(forced);
+  if (lane == 0) {
+    sh.red64[0][wave] = tot;
+    sh.red64[1][wave] = forced;
+  }
+  // state for the radix passes (read after the next barrier)
   if (tid == 0) {
-    const uint64_t target = (uint64_t)ceil(a.top_p * (double)tot);
-    sh.need = (int64_t)target - (int64_t)forced;
-    sh.prefix = 0;
     sh.above = 0;
     sh.all_optional = 0;
     sh.tie_mass = 0;
     sh.tie_keep = 0;
   }
+  // the digits start at the highest bit where optional keys differ
+  const uint32_t diff = kmin ^ kmax;
+  const int top = diff ? 31 - __clz(diff) : 0;        // highest differing bit
+  int width = min(kDigitBits, top + 1);
+  int shift = top + 1 - width;
+  const uint32_t common = (top == 31) ? 0u : (kmin & (0xFFFFFFFFu << (top + 1)));
+  if (tid == 0) sh.prefix = common;
+  for (int d = tid; d < (1 << width); d += kSelectThreads) {
+    sh.cnt[0][bslot(d)] = 0;
+    sh.mass[0][bslot(d)] = 0;
+  }
   __syncthreads();
-  const bool any_optional = sh.need > 0;
+  tot = 0;
+  forced = 0;
+  for (int w = 0; w < kSelectWaves; ++w) {
+    tot += sh.red64[0][w];
+    forced += sh.red64[1][w];
+  }
+  const uint64_t target = (uint64_t)ceil(a.top_p * (double)tot);
+  const int64_t need = (int64_t)target - (int64_t)forced;
+  const bool any_optional = need > 0 && kmin <= kmax;
 
-  // 3. radix select of the cutoff key over optional blocks, MSB digit first
+  // 3. radix select of the cutoff key over optional blocks, most significant
+  //    digit first; histogram buffers alternate (the next one is cleared
+  //    while the current one is built)
   if (any_optional) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int d = tid; d < 256; d += kSelectThreads) {
-        sh.cnt[d] = 0;
-        sh.mass[d] = 0;
-      }
-      __syncthreads();
-      const uint32_t hi_mask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int pass = 0;; ++pass) {
+      const int buf = pass & 1;
+      const uint32_t hi_mask = (shift + width >= 32) ? 0u : (0xFFFFFFFFu << (shift + width));
       const uint32_t prefix = sh.prefix;
+      const int next_width = min(kDigitBits, shift);
+      for (int d = tid; d < (1 << next_width) && shift > 0; d += kSelectThreads) {
+        sh.cnt[buf ^ 1][bslot(d)] = 0;
+        sh.mass[buf ^ 1][bslot(d)] = 0;
+      }
+      // counts are needed by the last digit only (tied blocks)
+      const bool last = shift == 0;
       for (int i = tid; i < nb; i += kSelectThreads) {
-        if (is_forced(i, L, G, a.sink, a.tail)) continue;
-        const float s = sc[i];
-        const uint32_t key = orderable(s);
+        uint32_t key;
+        uint64_t m;
+        if (!key_mass(i, key, m)) continue;
         if ((key & hi_mask) != (prefix & hi_mask)) continue;
-        const uint32_t d = (key >> shift) & 0xFFu;
-        atomicAdd(&sh.cnt[d], 1u);
-        atomicAdd((unsigned long long*)&sh.mass[d], (unsigned long long)mass_of(s, scale));
+        const int d = bslot((int)((key >> shift) & ((1u << width) - 1u)));
+        if (last) atomicAdd(&sh.cnt[buf][d], 1u);
+        atomicAdd((unsigned long long*)&sh.mass[buf][d], (unsigned long long)m);
       }
       __syncthreads();
-      if (wave == 0) pick_bucket(sh, shift);
+      if (wave == 0) pick_bucket(sh, buf, shift, width, (uint64_t)need);
       __syncthreads();
-      if (sh.all_optional) break;
+      if (sh.all_optional || shift == 0) break;
+      width = next_width;
+      shift -= width;
     }
   }
 
-  // 4. mask: forced, above the cutoff, or among the first tie_keep ties
+  // 4. mask: forced, above the cutoff, or among the first tie_keep ties;
+  //    thread t takes the contiguous run of blocks [t*run, (t+1)*run)
   const uint32_t vstar = sh.prefix;
   const bool keep_all = sh.all_optional != 0;
   const uint64_t tie_keep = sh.tie_keep;
+  const int run = (nb + kSelectThreads - 1) / kSelectThreads;
+  const int i0 = min(nb, tid * run), i1 = min(nb, i0 + run);
+  int my_ties = 0;
+  if (any_optional && !keep_all)
+    for (int i = i0; i < i1; ++i) {
+      uint32_t key;
+      uint64_t m;
+      my_ties += (key_mass(i, key, m) && key == vstar) ? 1 : 0;
+    }
+  // exclusive scan of the tie counts in thread (= block index) order
+  int incl = my_ties;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sh.redi[wave] = incl;
+  __syncthreads();
+  int64_t rank = incl - my_ties;
+  for (int w = 0; w < wave; ++w) rank += sh.redi[w];
   int kept_tokens = 0;
-  uint64_t ties_before = 0;  // ties at lower indices in earlier rounds
-  for (int base = 0; base < nb; base += kSelectThreads) {
-    const int i = base + tid;
-    bool keep = false, tie = false;
-    if (i < nb) {
-      const bool f = is_forced(i, L, G, a.sink, a.tail);
-      const uint32_t key = orderable(sc[i]);
-      tie = any_optional && !keep_all && !f && key == vstar;
-      keep = f || (any_optional && (keep_all || key > vstar));
-    }
-    // rank of this tie among ties in index order
-    const uint64_t bal = __ballot(tie);
-    const int below_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-    __syncthreads();
-    if (lane == 0) sh.redi[wave] = __popcll(bal);
-    __syncthreads();
-    int below_waves = 0, round_ties = 0;
-    for (int w = 0; w < kSelectWaves; ++w) {
-      if (w < wave) below_waves += sh.redi[w];
-      round_ties += sh.redi[w];
-    }
-    if (tie) keep = (ties_before + below_waves + below_in_wave) < tie_keep;
-    ties_before += round_ties;
-    if (i < nb) {
-      a.mask[cb0 + i] = keep ? 1 : 0;
-      if (keep) kept_tokens += min(i * G + G, L) - i * G;
-    }
+  for (int i = i0; i < i1; ++i) {
+    uint32_t key;
+    uint64_t m;
+    const bool opt = key_mass(i, key, m);
+    bool keep = !opt || (any_optional && (keep_all || key > vstar));
+    if (opt && any_optional && !keep_all && key == vstar) keep = (uint64_t)(rank++) < tie_keep;
+    a.mask[cb0 + i] = keep ? 1 : 0;
+    if (keep) kept_tokens += min(i * G + G, L) - i * G;
   }
   kept_tokens = wave_sum(kept_tokens);
-  __syncthreads();
+  __syncthreads();  // every wave has read redi
   if (lane == 0) sh.redi[wave] = kept_tokens;
   __syncthreads();
   if (tid == 0) {
@@ -269,6 +350,19 @@ __device__ void select_request(const SelectArgs& a, int req, SelectShared& sh) {
     for (int w = 0; w < kSelectWaves; ++w) s += sh.redi[w];
     a.kept[req] = s;
   }
+}
+
+// Selection of one request by the whole (kSelectThreads-thread) workgroup.
+// Uniform over the workgroup; every thread must call it.
+__device__ void select_request(const SelectArgs& a, int req, SelectShared& sh) {
+  const int nb = a.cu_blocks[req + 1] - a.cu_blocks[req];
+  if (nb <= 0) {
+    if (threadIdx.x == 0) a.kept[req] = 0;
+    return;
+  }
+  __syncthreads();  // the shared state may still be read by a previous call
+  if (nb <= kStageMax) select_impl<true>(a, req, nb, sh);
+  else select_impl<false>(a, req, nb, sh);
 }
 
 }  // namespace
