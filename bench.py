@@ -59,9 +59,13 @@ def parse_args():
     return ap.parse_args()
 
 
-def source_sha(name: str) -> str:
-    with open(os.path.join(CSRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(names) -> str:
+    """Hash of the source file(s) a kernel is built from."""
+    h = hashlib.sha256()
+    for name in ([names] if isinstance(names, str) else names):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str, src: str, launches_per_call: int = 1):
@@ -85,7 +89,7 @@ TRAFFIC_KERNELS = {
     "up_compact_scan_kernel": ("up_compact.hip", r"\bup_compact_scan_kernel\b"),
     "up_rowstats_kernel": ("up_score.hip", r"\bup_rowstats_kernel\b"),
     "up_colsum_kernel": ("up_score.hip", r"\bup_colsum_kernel\b"),
-    "up_select_kernel": ("up_select.hip", r"\bup_select_kernel\b"),
+    "up_select_kernel": (("up_select.hip", "up_select_impl.h"), r"\bup_select_kernel\b"),
     "up_rowop_kernel_norm": ("up_compact.hip", r"\bup_rowop_kernel<0, "),
     "up_rowop_kernel_add": ("up_compact.hip", r"\bup_rowop_kernel<1, "),
 }
@@ -122,7 +126,8 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
             vals = [x for n, v in per.items() if re.search(pat, n) for x in v]
             if not vals:
                 continue
-            rec = out.setdefault(short, {"source_sha": source_sha(src), "source": src})
+            rec = out.setdefault(short, {"source_sha": source_sha(src),
+                                         "source": src if isinstance(src, str) else "+".join(src)})
             rec[key + "_bytes_per_launch"] = sum(vals) / len(vals) * scale
             rec[key + "_scale"] = scale
             rec[key + "_raw_kib_per_launch"] = sum(vals) / len(vals) / 1024.0

@@ -68,3 +68,67 @@ def test_packed_batch16():
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_qwen3next_sweep(n, G):
     _full(f"qwen3next_L131072_n{n}_G{G}")
+
+
+def test_fused_pipeline_full_size():
+    """The fused pipeline at the benchmark's full size (one 131072-token
+    request, hidden 4096 bf16): the selecting epilogue gives bit-identical
+    scores, mask and kept counts to the two calls; the normalised operand
+    and the residual sum are checked against the oracle on 1024 sampled kept
+    rows (operand within half a bf16 ulp plus the fp32 error bound, residual
+    sum exact), positions and cu_seqlens_out exactly."""
+    import token_block_sparsification_amd as U
+    from _parity import bf16_to_f64, check_rounded
+    w = W.get_workload("llama8b_L131072")
+    dev = torch.device("cuda")
+    inp = W.make_inputs(w, device=dev)
+    cu = inp["cu_seqlens"].cpu()
+    batch = U.Batch.make(cu, w.block, dev)
+    q, k, hidden, pos = inp["q"], inp["k"], inp["hidden"], inp["positions"]
+    ws = U.Workspace.make(batch, w.hq, w.hkv, w.head_dim, w.n_query, hidden, dev)
+    T, N, B = batch.num_tokens, batch.num_blocks, batch.num_seqs
+    outs = []
+    for fused in (False, True):
+        bs = torch.empty(N, device=dev)
+        mask = torch.empty(N, dtype=torch.uint8, device=dev)
+        kept = torch.empty(B, dtype=torch.int32, device=dev)
+        if fused:
+            U.up_score_select(cu, batch.cu_seqlens_d, batch.cu_blocks_d, q, k, w.n_query, w.block,
+                              0.0, None, bs, w.top_p, w.sink, w.tail, mask, kept, ws.score_ws)
+        else:
+            U.up_score(cu, batch.cu_seqlens_d, batch.cu_blocks_d, q, k, w.n_query, w.block, 0.0,
+                       None, bs, ws.score_ws)
+            U.up_select_topp(cu, batch.cu_seqlens_d, batch.cu_blocks_d, bs, w.block, w.top_p,
+                             w.sink, w.tail, mask, kept)
+        outs.append((bs, mask, kept))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    mask = outs[1][1]
+    D = hidden.shape[1]
+    normed = torch.empty((T, D), dtype=hidden.dtype, device=dev)
+    pout = torch.empty(T, dtype=torch.int32, device=dev)
+    cu_out = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    U.up_compact_rmsnorm(cu, batch.cu_seqlens_d, batch.cu_blocks_d, w.block, mask, hidden, None,
+                         1e-6, pos, normed, None, pout, cu_out, ws.compact_ws)
+    mask_np = mask.cpu().numpy()
+    keep_idx = np.flatnonzero(O.token_keep(mask_np, cu.numpy(), w.block))
+    n = len(keep_idx)
+    delta = torch.randn((n, D), device=dev).to(hidden.dtype)
+    out = torch.empty((n, D), dtype=hidden.dtype, device=dev)
+    U.up_gather_add(cu, batch.cu_seqlens_d, batch.cu_blocks_d, w.block, mask, hidden, delta, out,
+                    ws.compact_ws)
+    torch.cuda.synchronize()
+    _, _, cu_ref = O.compact(mask_np, np.zeros((T, 1)), np.zeros(T), cu.numpy(), w.block)
+    assert list(cu_out.cpu().numpy()) == list(cu_ref)
+    assert np.array_equal(pout[:n].cpu().numpy(), pos.cpu().numpy()[keep_idx])
+    rows = np.sort(np.random.default_rng(5).choice(n, size=1024, replace=False))
+    src = torch.from_numpy(keep_idx[rows]).to(dev)
+    sel = torch.from_numpy(rows).to(dev)
+    h64 = bf16_to_f64(hidden.index_select(0, src))
+    y = O.rms_normalize(h64, None, 1e-6)
+    frac = check_rounded(bf16_to_f64(normed.index_select(0, sel)), y, "bf16",
+                         (D / 64 + 16) * 2.0 ** -24, "normed operand")
+    exp = O.round_to_format(h64 + bf16_to_f64(delta.index_select(0, sel)), "bf16")
+    assert np.array_equal(bf16_to_f64(out.index_select(0, sel)), exp)
+    print(f"[fullsize] fused pipeline: kept={n} exactly_rounded={frac:.4f}", flush=True)
