@@ -80,6 +80,17 @@ def test_large_n_and_head_dims(n, G, d):
     _end_to_end(W.make_inputs(w), n, G, name=w.name)
 
 
+@pytest.mark.parametrize("hq,hkv,d,n", [(64, 2, 128, 128), (1024, 1, 64, 8), (48, 3, 256, 100)])
+def test_wide_query_groups(hq, hkv, d, n):
+    """Many query heads per KV head: r*n rows per KV group span several
+    row groups in both passes (up to 8192 rows), and hq at its 1024 limit."""
+    lengths = (3000, 200, 0, 1300) if hq < 1024 else (600, 9, 250)
+    w = W.Workload(name=f"wide_hq{hq}_hkv{hkv}_d{d}", lengths=lengths, hq=hq, hkv=hkv, head_dim=d,
+                   hidden_dim=32, hidden_dtype="bf16", seed=5900 + hq + d, plant_frac=0.05,
+                   n_query=n, block=64, num_seqs=len(lengths))
+    _end_to_end(W.make_inputs(w), n, 64, name=w.name)
+
+
 def test_tail_equals_n_and_small_p():
     w = W.Workload(name="p_sweep", lengths=(4096, 2000), hq=8, hkv=2, head_dim=128, hidden_dim=32,
                    hidden_dtype="bf16", seed=6001, plant_frac=0.1, num_seqs=2)
