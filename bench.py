@@ -317,6 +317,29 @@ def main():
     U.up_history_init(ledger, B, cap)
     del normed, delta
 
+    # The same step captured once as a HIP graph and replayed: the kernels
+    # without the host's per-call work (validation, launches).
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(layer=0)   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(layer=1)
+    U.up_history_init(ledger, B, cap)
+    gm = new_marks(["graph"])
+    torch.cuda.synchronize()
+    gm["graph"][0].record()
+    for _ in range(nb):
+        graph.replay()
+    gm["graph"][1].record()
+    torch.cuda.synchronize()
+    graph_step_us = gm["graph"][0].elapsed_time(gm["graph"][1]) * 1e3 / nb
+    del graph
+    U.up_history_init(ledger, B, cap)
+
     ms_per_step = (t1 - t0) * 1e3 / K
     per_call_us = {n: mean_us(brk, n) for n in calls}
     per_call_us[dominant] = dominant_us
@@ -427,6 +450,7 @@ def main():
                        load_traffic("up_revive_copy_kernel", "up_compact.hip"),
                        load_traffic("up_compact_scan_kernel", "up_compact.hip"))},
         "kv_len_us": round(mean_us(rv_marks, "up_kv_len"), 2),
+        "graph_step_us": round(graph_step_us, 2),
         "fused_pipeline": fused_rec,
         "keep_ratio": round(kept / T, 5),
         "input_generation_s": round(t_gen, 2),

@@ -770,13 +770,8 @@ up_colsum_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 // Epilogue: token score = fixed-order sum of the per-(KV head, row group)
 // partials; block score = mean over the block's tokens.  One wave per block.
-// SELECT (fused pipeline): each workgroup then counts its blocks into their
-// requests' arrival counters; the workgroup that completes a request runs
-// that request's Top-p selection (select_request) on the block scores, so
-// no separate selection launch is needed.  Every wave fences its block score
-// (device scope) before the count, and the selecting workgroup fences
-// before reading, so it sees every block score of the request whichever XCD
-// wrote it.
+// The fused pipeline's variant (up_blockmean_select_kernel, below) also runs
+// the Top-p selection in the workgroup that completes a request.
 // ---------------------------------------------------------------------------
 // One wave per block score; writes it unless `score` is given (then the
 // caller stores it).
