@@ -55,6 +55,9 @@ MUTATIONS = {
     "rms_gain_dropped": ("y = y * np.asarray(gamma, dtype=np.float64)[None, :]", "y = y"),
     "compact_rmsnorm_gain_dropped": ("return rms_normalize(h, gamma, eps), p_out, cu_out",
                                      "return rms_normalize(h, None, eps), p_out, cu_out"),
+    "band_one_sided": ("if c1 >= p - eps and c0 <= p + eps:", "if c1 >= p + eps and c0 <= p + eps:"),
+    "trace_forced_mass_ignored": ("acc = float(sum(float(bs[b]) for b in range(len(bs)) if forced[b]))",
+                                  "acc = 0.0"),
     "gather_add_sign": ("return round_to_format(h + d, fmt)", "return round_to_format(h - d, fmt)"),
     "gather_add_delta_shifted": ("d = np.asarray(delta, dtype=np.float64)[: len(h)]",
                                  "d = np.asarray(delta, dtype=np.float64)[1: len(h) + 1]"),

@@ -416,6 +416,26 @@ def check_widen_bf16():
     np.testing.assert_array_equal(O.widen_bf16(x.view(torch.int16).numpy()), x.to(torch.float64).numpy())
 
 
+def check_knife_edge_band():
+    """The parity rule's band, on a hand-worked request: G = 1, no forced
+    blocks, scores 4, 3, 2, 1 (total 10) give cumulative fractions 0.4, 0.7,
+    0.9, 1.0 in (score desc) order; at p = 0.7 the blocks whose interval
+    meets [p - 1e-4, p + 1e-4] are the second and third; at p = 0.55 only the
+    second; with blocks 0 and 3 forced (sink 1, tail 1) the optional order
+    starts from their mass fraction 0.4."""
+    bs = np.array([1.0, 4.0, 2.0, 3.0])          # block index order; ranks 3, 0, 2, 1
+    order, c0, c1, forced = O.selection_trace(bs, 4, 1, 0.7, 0, 0)
+    assert order == [1, 3, 2, 0] and not forced.any()
+    np.testing.assert_allclose(c0, [0.0, 0.4, 0.7, 0.9])
+    np.testing.assert_allclose(c1, [0.4, 0.7, 0.9, 1.0])
+    assert list(np.flatnonzero(O.band_blocks(bs, 4, 1, 0.7, 0, 0))) == [2, 3]
+    assert list(np.flatnonzero(O.band_blocks(bs, 4, 1, 0.55, 0, 0))) == [3]
+    order, c0, c1, forced = O.selection_trace(bs, 4, 1, 0.7, 1, 1)
+    assert list(np.flatnonzero(forced)) == [0, 3] and order == [1, 2]
+    np.testing.assert_allclose(c0, [0.4, 0.8])
+    np.testing.assert_allclose(c1, [0.8, 1.0])
+
+
 def check_round_to_format():
     """Rounding to a binary format agrees with library conversions that round
     once, directly from the wider value: numpy's fp64 -> fp32 and fp64 -> f16
@@ -522,7 +542,8 @@ ALL_CHECKS = [
     check_gqa_peak, check_head_additivity, check_n1_textbook_softmax, check_block_means,
     check_select_golden, check_one_hot, check_uniform_ceil, check_select_invariants,
     check_brute_force, check_scale_invariance, check_concentration, check_short_requests,
-    check_compaction, check_revival, check_history, check_widen_bf16, check_round_to_format,
+    check_compaction, check_revival, check_history, check_widen_bf16, check_knife_edge_band,
+    check_round_to_format,
     check_rmsnorm, check_compact_rmsnorm, check_gather_add,
 ]
 
