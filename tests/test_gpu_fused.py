@@ -155,6 +155,8 @@ SEL_CASES = [
     ("many_small_d64", dict(lengths=tuple([17, 0, 40, 33] * 40), hq=4, hkv=4, head_dim=64,
                             n_query=32, block=16)),
     ("long_d256", dict(lengths=(20000, 3000), hq=16, hkv=2, head_dim=256, n_query=128, block=128)),
+    # a request of 4375 blocks: more than the selection stages in LDS
+    ("many_blocks_d64", dict(lengths=(70000, 100), hq=2, hkv=1, head_dim=64, n_query=16, block=16)),
 ]
 
 
