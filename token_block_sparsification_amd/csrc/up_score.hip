@@ -807,11 +807,10 @@ __device__ __forceinline__ int blockmean_one(const ScoreArgs& a, int64_t b, int 
   return r;
 }
 
-// Blocks per workgroup of the selecting epilogue (UP_SEL_BPW / 4 per wave).
-#ifndef UP_SEL_BPW
-#define UP_SEL_BPW 4
-#endif
-constexpr int kSelBlocksPerWg = UP_SEL_BPW;
+// Blocks per workgroup of the selecting epilogue: one per wave.
+constexpr int kSelBlocksPerWg = 16;
+constexpr int kSelEpilogueThreads = 64 * kSelBlocksPerWg;
+static_assert(kSelEpilogueThreads >= kSelectThreads, "the selection runs on the first waves");
 
 __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -819,14 +818,16 @@ __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
   if (b < a.num_blocks) blockmean_one(a, b, lane);
 }
 
-// Fused selection: each workgroup computes kSelBlocksPerWg block scores (its
-// four waves share them out) into LDS; wave 0 stores them, releases them at
-// device scope
-// (its own stores, one fence per workgroup) and adds the workgroup's blocks
-// to each touched request's arrival counter.  The workgroup that completes a
-// request acquires at device scope and runs that request's Top-p selection
-// (select_request) on the block scores, whichever XCD wrote them.
-__global__ void __launch_bounds__(256) up_blockmean_select_kernel(ScoreArgs a, SelectArgs sa) {
+// Fused selection: each workgroup computes 16 block scores (one per wave)
+// into LDS; wave 0 stores them, releases them at device scope (its own
+// stores, one fence per workgroup) and adds the workgroup's blocks to each
+// touched request's arrival counter.  The workgroup that completes a request
+// acquires at device scope and its first kSelectThreads threads run that
+// request's Top-p selection (select_request) on the block scores, whichever
+// XCD wrote them; its other waves have ended by then (a barrier waits only
+// for the waves still running).
+__global__ void __launch_bounds__(kSelEpilogueThreads)
+up_blockmean_select_kernel(ScoreArgs a, SelectArgs sa) {
   __shared__ SelectShared sh;
   __shared__ int s_req[kSelBlocksPerWg];
   __shared__ float s_score[kSelBlocksPerWg];
@@ -834,14 +835,12 @@ __global__ void __launch_bounds__(256) up_blockmean_select_kernel(ScoreArgs a, S
   __shared__ int s_nsel;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t b0 = (int64_t)blockIdx.x * kSelBlocksPerWg;
-#pragma unroll
-  for (int i = 0; i < kSelBlocksPerWg / 4; ++i) {
-    const int slot = wave * (kSelBlocksPerWg / 4) + i;
+  {
     float sc = 0.f;
-    const int r = b0 + slot < a.num_blocks ? blockmean_one(a, b0 + slot, lane, &sc) : -1;
+    const int r = b0 + wave < a.num_blocks ? blockmean_one(a, b0 + wave, lane, &sc) : -1;
     if (lane == 0) {
-      s_req[slot] = r;
-      s_score[slot] = sc;
+      s_req[wave] = r;
+      s_score[wave] = sc;
     }
   }
   __syncthreads();
@@ -866,7 +865,7 @@ __global__ void __launch_bounds__(256) up_blockmean_select_kernel(ScoreArgs a, S
   }
   __syncthreads();
   const int nsel = s_nsel;
-  if (nsel == 0) return;  // uniform
+  if (nsel == 0 || threadIdx.x >= kSelectThreads) return;  // whole waves
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int i = 0; i < nsel; ++i) select_request(sa, s_sel[i], sh);
 }
@@ -1143,8 +1142,8 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
       const up::SelectArgs sa{cu_seqlens_d, cu_blocks_d, block_scores, sel->block_mask,
                               sel->kept_tokens, block, sel->sink, sel->tail, sel->top_p};
       hipLaunchKernelGGL(up::up_blockmean_select_kernel,
-                         dim3((unsigned)up::ceil_div(N, up::kSelBlocksPerWg)), dim3(256), 0, stream,
-                         a, sa);
+                         dim3((unsigned)up::ceil_div(N, up::kSelBlocksPerWg)),
+                         dim3(up::kSelEpilogueThreads), 0, stream, a, sa);
       st = up::check_launch("up_blockmean_select_kernel");
     } else {
       hipLaunchKernelGGL(up::up_blockmean_kernel, dim3((unsigned)up::ceil_div(N, 4)), dim3(256), 0,
