@@ -452,7 +452,9 @@ __global__ void __launch_bounds__(kCompactThreads) up_rowop_kernel(RowOpArgs a) 
       if (r >= rows) continue;
       const u32x4_t* s = reinterpret_cast<const u32x4_t*>(a.src + (int64_t)(src + r) * a.src_stride);
       const u32x4_t* d =
-          reinterpret_cast<const u32x4_t*>(a.delta + (int64_t)(dst + r) * a.delta_stride);
+          OP == kOpAdd
+              ? reinterpret_cast<const u32x4_t*>(a.delta + (int64_t)(dst + r) * a.delta_stride)
+              : nullptr;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         const int64_t c = lane + 64 * v;
