@@ -321,6 +321,26 @@ __device__ __forceinline__ void interleave_hint() {
   }
 }
 
+// The same with one LDS read after each MFMA (a group that rolls in the next
+// key sub-tile's fragments).
+template <int D>
+__device__ __forceinline__ void interleave_hint_roll() {
+  constexpr int kSlots = D / 16 / UP_IL_MFMA;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, UP_IL_MFMA, 0);          // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, UP_IL_MFMA, 0);          // DS read
+    __builtin_amdgcn_sched_group_barrier(0x402, UP_IL_VALU / kSlots, 0);  // VALU or TRANS
+  }
+}
+
+// Fragment s of key sub-tile `sub` (32 keys) of an LDS tile.
+template <int D, int W>
+__device__ __forceinline__ bf16x8_t load_frag(const uint16_t* tile, int sub, int lane, int s) {
+  using Tile = KTile<D, W>;
+  return load_bf16x8(tile + Tile::offset(sub * 32 + (lane & 31), 2 * s + (lane >> 5)));
+}
+
 template <int D, int W>
 __device__ __forceinline__ void load_frags(const uint16_t* tile, int sub, int lane,
                                            bf16x8_t (&f)[D / 16]) {
@@ -363,7 +383,9 @@ __device__ __forceinline__ void rowstats_update(f32x16_t acc, int t, bool masked
 
 // One LDS tile: NG = (KT/32)*NT groups, ordered (mt, t).  On entry acc holds
 // the (issued) S of group 0 of this tile and af the A fragments of mt = 0;
-// on exit they hold group 0 of the next tile (from `nxt`).
+// on exit they hold group 0 of the next tile (from `nxt`).  The pipelined
+// form with NT >= 2 reads each sub-tile's fragments while the previous
+// sub-tile's last group issues, so no MFMA waits on its LDS read.
 template <int D, int NT, int W, bool MASKED, bool PIPE>
 __device__ __forceinline__ void rowstats_iter(const uint16_t* cur, const uint16_t* nxt, int tkey0,
                                               int key1, int lane, float C,
@@ -387,23 +409,43 @@ __device__ __forceinline__ void rowstats_iter(const uint16_t* cur, const uint16_
     }
     return;
   }
+  constexpr int SPT = KT / 32;
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     const int mt = q / NT, t = q % NT;
+    const int mt1 = (q + 1) / NT, t1 = (q + 1) % NT;  // group q+1; mt1 == SPT: next tile
     f32x16_t nacc = {};
-    if (q + 1 < NG) {
-      const int mt1 = (q + 1) / NT, t1 = (q + 1) % NT;
-      if (mt1 != mt) load_frags<D, W>(cur, mt1, lane, af);
+    if constexpr (NT >= 2) {
+      // Rolling fragments: af holds sub-tile mt1 already.  When group q+1 is
+      // the last user of its sub-tile, each fragment is replaced by the next
+      // sub-tile's (of this tile, else sub-tile 0 of the next) right after
+      // the MFMA that reads it, a whole group ahead of its first use.
+      const bool roll = t1 == NT - 1;
+      const int ns = mt1 + 1;
+      const uint16_t* src = ns < SPT ? cur : nxt;
+      const int nsub = ns < SPT ? ns : 0;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) nacc = mfma32(af[s], qf[t1][s], nacc);
+      for (int s = 0; s < D / 16; ++s) {
+        nacc = mfma32(af[s], qf[t1][s], nacc);
+        if (roll) af[s] = load_frag<D, W>(src, nsub, lane, s);
+      }
+      rowstats_update<NT>(acc, t, MASKED, tkey0 + mt * 32, key1, lane, C, ipos, m_run, l_run);
+      acc = nacc;
+      if (roll) interleave_hint_roll<D>(); else interleave_hint<D>();
     } else {
-      load_frags<D, W>(nxt, 0, lane, af);
+      if (q + 1 < NG) {
+        if (mt1 != mt) load_frags<D, W>(cur, mt1, lane, af);
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) nacc = mfma32(af[s], qf[0][s], nacc);
+        for (int s = 0; s < D / 16; ++s) nacc = mfma32(af[s], qf[t1][s], nacc);
+      } else {
+        load_frags<D, W>(nxt, 0, lane, af);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) nacc = mfma32(af[s], qf[0][s], nacc);
+      }
+      rowstats_update<NT>(acc, t, MASKED, tkey0 + mt * 32, key1, lane, C, ipos, m_run, l_run);
+      acc = nacc;
+      interleave_hint<D>();
     }
-    rowstats_update<NT>(acc, t, MASKED, tkey0 + mt * 32, key1, lane, C, ipos, m_run, l_run);
-    acc = nacc;
-    if (PIPE) interleave_hint<D>();
   }
 }
 
@@ -637,6 +679,52 @@ __device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t*
   }
 }
 
+// Mask-free tile with the key fragments double-buffered: the fragments of the
+// next key sub-tile are read from LDS one group ahead of the MFMAs that use
+// them (kf[p] holds the sub-tiles of parity p), so no MFMA waits on its LDS
+// read.  Needs an even number of sub-tiles per tile (the parity of a sub-tile
+// is then the same in the current and the next tile).  On entry acc holds
+// the issued S of group 0, kf[0] / kf[1] sub-tiles 0 / 1 of this tile; on exit
+// the same for the next tile.
+template <int D, int NT, int W>
+__device__ __forceinline__ void colsum_iter_db(const uint16_t* cur, const uint16_t* nxt, int tkey0,
+                                               int key1, int lane, int wave, int row0, int R,
+                                               int n_eff, int qpos0, float C,
+                                               const bf16x8_t (&qf)[NT][D / 16],
+                                               const float (&bv)[NT][16], float (*colrow)[64],
+                                               f32x16_t& acc, bf16x8_t (&kf)[2][D / 16]) {
+  constexpr int KT = KTile<D, W>::KT;
+  constexpr int SPT = KT / 32;
+  constexpr int NG = SPT * NT;
+  static_assert(SPT % 2 == 0, "double-buffered fragments need an even sub-tile count");
+  float col = 0.f;
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int nt = q / NT, t = q % NT;
+    const int nt1 = (q + 1) / NT, t1 = (q + 1) % NT;  // group q+1; nt1 == SPT: next tile
+    if (t1 == 0) {
+      // group q+1 opens sub-tile nt1, whose fragments are resident: read the
+      // one after it into the buffer its predecessor (last used by the MFMAs
+      // issued in the previous group) frees
+      const int ps = nt1 + 1;
+      if (ps < SPT) load_frags<D, W>(cur, ps, lane, kf[ps & 1]);
+      else load_frags<D, W>(nxt, ps - SPT, lane, kf[ps & 1]);
+    }
+    f32x16_t nacc = {};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) nacc = mfma32(qf[t1][s], kf[nt1 & 1][s], nacc);
+    const int key = tkey0 + nt * 32 + (lane & 31);
+    col += colsum_update<NT>(acc, t, false, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
+    if (t == NT - 1) {
+      col = sum_halves(col);
+      colrow[wave][nt * 32 + (lane & 31)] = col;  // both halves hold the same sum
+      col = 0.f;
+    }
+    acc = nacc;
+    interleave_hint<D>();
+  }
+}
+
 // Column partials of a finished tile (its waves' sums in colrow, complete
 // after the tile's ring barrier): every wave adds the W wave sums, in wave
 // order, for its KT/W keys and writes them.  All 64 lanes run it; lanes that
@@ -711,12 +799,15 @@ up_colsum_kernel(ScoreArgs a) {
   // a fixed wait, then the last mask-free tiles, then the masked tiles.
   const int nfull = (key1 - key0) / KT;
   const int nmain = max(0, min(nfast, nfull - 3));
-  bf16x8_t kf[D / 16];
+  constexpr bool DB = PIPE && (KT / 32) % 2 == 0;  // double-buffered fragments
+  bf16x8_t kfb[DB ? 2 : 1][D / 16];
+  auto& kf = kfb[0];
   int it = 0;
   if (nfast > 0) {
     f32x16_t acc = {};
     if constexpr (PIPE) {
       load_frags<D, W>(kl[0], 0, lane, kf);
+      if constexpr (DB) load_frags<D, W>(kl[0], 1, lane, kfb[DB ? 1 : 0]);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) acc = mfma32(qf[0][s], kf[s], acc);
     }
@@ -729,9 +820,13 @@ up_colsum_kernel(ScoreArgs a) {
       if (it + U > 0)
         colsum_flush<W, KT, true>(colbuf[(U + 1) & 1], wave, lane, key0 + (it + U - 1) * KT, key1,
                                   colout);
-      colsum_iter<D, NT, W, false, PIPE>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1,
-                                         lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
-                                         colbuf[U & 1], acc, kf);
+      if constexpr (DB)
+        colsum_iter_db<D, NT, W>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1, lane,
+                                 wave, row0, R, n_eff, qpos0, C, qf, bv, colbuf[U & 1], acc, kfb);
+      else
+        colsum_iter<D, NT, W, false, PIPE>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1,
+                                           lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
+                                           colbuf[U & 1], acc, kf);
       ring_step<Tile, true>();
     };
     for (; it + kRing <= nmain; it += kRing) {
@@ -745,9 +840,13 @@ up_colsum_kernel(ScoreArgs a) {
       if (it > 0)
         colsum_flush<W, KT, false>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT, key1,
                                    colout);
-      colsum_iter<D, NT, W, false, PIPE>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1,
-                                         lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
-                                         colbuf[it & 1], acc, kf);
+      if constexpr (DB)
+        colsum_iter_db<D, NT, W>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1, lane,
+                                 wave, row0, R, n_eff, qpos0, C, qf, bv, colbuf[it & 1], acc, kfb);
+      else
+        colsum_iter<D, NT, W, false, PIPE>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT,
+                                           key1, lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
+                                           colbuf[it & 1], acc, kf);
       if (it + 3 < ntiles) ring_step<Tile, true>(); else ring_step<Tile, false>();
     }
   }
