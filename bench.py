@@ -340,6 +340,8 @@ def main():
     del graph
     U.up_history_init(ledger, B, cap)
 
+    measured = measured_peaks(dev)
+
     ms_per_step = (t1 - t0) * 1e3 / K
     per_call_us = {n: mean_us(brk, n) for n in calls}
     per_call_us[dominant] = dominant_us
@@ -437,10 +439,14 @@ def main():
                        "algorithmic_tflops": round(score_tflops_alg, 1),
                        "frac_of_peak_executed": round(score_tflops_exec / PEAK_BF16_TFLOPS, 4),
                        "frac_of_peak_algorithmic": round(score_tflops_alg / PEAK_BF16_TFLOPS, 4),
+                       "frac_of_measured_gemm_executed": round(score_tflops_exec / measured["gemm_bf16_tflops"], 4),
                        "executed_flops_per_call": flops_exec, "k_bytes_per_call": int(score_bytes)},
         "select_compact_hbm": {"bytes": int(compact_bytes + 5 * N),
                                "gbs": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9, 1),
-                               "frac_of_peak": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9 / PEAK_HBM_GBS, 4)},
+                               "frac_of_peak": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9 / PEAK_HBM_GBS, 4),
+                               "frac_of_measured_copy": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9
+                                                              / measured["copy_gbs"], 4)},
+        "measured_peaks": measured,
         "revive": {"us": round(mean_us(rv_marks, "up_revive"), 2),
                    "gbs": round(compact_bytes_rv / (mean_us(rv_marks, "up_revive") * 1e-6) / 1e9, 1),
                    "frac_of_hbm_peak": round(compact_bytes_rv / (mean_us(rv_marks, "up_revive") * 1e-6)
@@ -459,6 +465,41 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["parity"] = cpu_leg(w, inp, ws, kept, args.cpu_threads, T)
     print(json.dumps(rec), flush=True)
+
+
+def measured_peaks(dev) -> dict:
+    """What library code reaches on this GPU, as a second yardstick beside the
+    datasheet peaks: a device-to-device copy of 1 GiB (bytes read + written)
+    and a bf16 GEMM of 8192^3 through torch.matmul (hipBLASLt)."""
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    t_gemm = timed(lambda: torch.matmul(a, b, out=c), 10)
+    del a, b, c
+    torch.cuda.synchronize()
+    return {"copy_gbs": round(2 * COPY_BYTES / t_copy / 1e9, 1),
+            "gemm_bf16_tflops": round(2.0 * n ** 3 / t_gemm / 1e12, 1),
+            "note": "torch device-to-device copy of 1 GiB (read + write bytes) and torch.matmul "
+                    "bf16 8192x8192x8192 (hipBLASLt), timed with HIP events after the steps"}
 
 
 def stack_bench(args, dev):
