@@ -1058,13 +1058,18 @@ extern "C" up_status up_score_workspace_size(int num_seqs, const int32_t* cu_seq
 namespace {
 
 #ifndef UP_CK_MAX
-#define UP_CK_MAX 2048
+#define UP_CK_MAX 4096
 #endif
 #ifndef UP_MIN_WGS
-#define UP_MIN_WGS 1024
+#define UP_MIN_WGS 512
 #endif
 // Key chunk per workgroup: the largest power of two in [256, UP_CK_MAX] that
-// still gives >= UP_MIN_WGS workgroups for this batch.
+// still gives >= UP_MIN_WGS workgroups for this batch.  512 is one resident
+// round on the 256 CUs of gfx950 (two row-statistics workgroups per CU, and
+// half as many column-sum workgroups at one per CU): longer chunks cost less
+// per key (ring fill, Q loads, chunk merges) as long as every CU has work.
+// Measured against 2048-key chunks with >= 1024 workgroups: 15% less
+// scoring time at L = 32K, 3% less at 128K.
 int choose_ck(int num_seqs, const int32_t* cu_h, int hkv, int rg) {
   int ck = UP_CK_MAX;
   while (ck > 256) {
