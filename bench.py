@@ -18,6 +18,7 @@ check of the GPU result against it).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -41,6 +42,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_L131072")
+    ap.add_argument("--tail", type=int, default=None,
+                    help="override the always-kept tail tokens (-1: the workload's n_query)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (for profiler runs)")
     ap.add_argument("--cpu-threads", type=int, default=1,
@@ -164,6 +167,8 @@ def main():
         return
 
     w = W.get_workload(args.workload)
+    if args.tail is not None:
+        w = w.with_(tail=args.tail if args.tail >= 0 else w.n_query)
     t_gen = time.perf_counter()
     inp = W.make_inputs(w, device=dev)
     torch.cuda.synchronize()
@@ -208,6 +213,15 @@ def main():
 
     def mean_us(marks_list, name):
         return float(np.mean([m[name][0].elapsed_time(m[name][1]) for m in marks_list])) * 1e3
+
+    def med_us(marks_list, name):
+        """Median: the side measurements below are robust to one host stall
+        (the GPU idles inside an event bracket while the host is held up)."""
+        return float(np.median([m[name][0].elapsed_time(m[name][1]) for m in marks_list])) * 1e3
+
+    # No garbage-collector pauses while anything is timed.
+    gc.collect()
+    gc.disable()
 
     # Warm-up; its last steps bracket every call to find the dominant one.
     warm_marks = []
@@ -268,8 +282,10 @@ def main():
     # packed rows written back over the full buffer; here they are unchanged,
     # so `hidden` keeps its bytes) and the ledger read-back.
     kv_len = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    # Each side loop below runs one extra, discarded first iteration: a
+    # first call can stall the host (lazy kernel loading) inside its events.
     rv_marks = []
-    for i in range(nb):
+    for i in range(nb + 1):
         m = new_marks(["up_revive", "up_kv_len"])
         m["up_revive"][0].record()
         U.up_revive(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, w.block,
@@ -278,7 +294,8 @@ def main():
         m["up_kv_len"][0].record()
         U.up_kv_len(ledger, B, cap, 1 << 20, batch.cu_seqlens_d, kv_len)
         m["up_kv_len"][1].record()
-        rv_marks.append(m)
+        if i:
+            rv_marks.append(m)
     torch.cuda.synchronize()
 
     # Fused pipeline, outside the timed region: selection in the scoring
@@ -289,7 +306,7 @@ def main():
     normed = torch.empty((T, D), dtype=hidden.dtype, device=dev)
     delta = torch.randn((max(kept, 1), D), device=dev).to(hidden.dtype)
     fz = []
-    for i in range(nb):
+    for i in range(nb + 1):
         m = new_marks(["up_score_select", "up_compact_rmsnorm", "up_gather_add", "torch_rmsnorm",
                        "chain_fused"])
         m["chain_fused"][0].record()
@@ -312,7 +329,8 @@ def main():
         m["torch_rmsnorm"][0].record()
         torch.nn.functional.rms_norm(ws.hidden_out[:kept], (D,), eps=1e-6)
         m["torch_rmsnorm"][1].record()
-        fz.append(m)
+        if i:
+            fz.append(m)
     torch.cuda.synchronize()
     U.up_history_init(ledger, B, cap)
     del normed, delta
@@ -341,9 +359,10 @@ def main():
     U.up_history_init(ledger, B, cap)
 
     measured = measured_peaks(dev)
+    gc.enable()
 
     ms_per_step = (t1 - t0) * 1e3 / K
-    per_call_us = {n: mean_us(brk, n) for n in calls}
+    per_call_us = {n: med_us(brk, n) for n in calls}
     per_call_us[dominant] = dominant_us
     tokens_per_s = T / (ms_per_step / 1e3)
 
@@ -386,7 +405,7 @@ def main():
                     "traffic": None, "algorithmic_flops_per_launch": flops_exec}
 
     # fused pipeline figures
-    fz_us = {n: mean_us(fz, n) for n in fz[0]}
+    fz_us = {n: med_us(fz, n) for n in fz[0]}
     norm_bytes = 2 * kept * row_bytes + 2 * 4 * kept + N     # kept rows read, operand written
     add_bytes = 3 * kept * row_bytes + N                      # frozen + delta read, sum written
     unfused_chain_us = sum(per_call_us[n] for n in calls) + fz_us["torch_rmsnorm"]
@@ -447,15 +466,15 @@ def main():
                                "frac_of_measured_copy": round((compact_bytes + 5 * N) / (t_select + t_compact) / 1e9
                                                               / measured["copy_gbs"], 4)},
         "measured_peaks": measured,
-        "revive": {"us": round(mean_us(rv_marks, "up_revive"), 2),
-                   "gbs": round(compact_bytes_rv / (mean_us(rv_marks, "up_revive") * 1e-6) / 1e9, 1),
-                   "frac_of_hbm_peak": round(compact_bytes_rv / (mean_us(rv_marks, "up_revive") * 1e-6)
+        "revive": {"us": round(med_us(rv_marks, "up_revive"), 2),
+                   "gbs": round(compact_bytes_rv / (med_us(rv_marks, "up_revive") * 1e-6) / 1e9, 1),
+                   "frac_of_hbm_peak": round(compact_bytes_rv / (med_us(rv_marks, "up_revive") * 1e-6)
                                              / 1e9 / PEAK_HBM_GBS, 4),
                    "algorithmic_bytes": int(compact_bytes_rv),
                    "traffic": (lambda a, b: a + b if a is not None and b is not None else None)(
                        load_traffic("up_revive_copy_kernel", "up_compact.hip"),
                        load_traffic("up_compact_scan_kernel", "up_compact.hip"))},
-        "kv_len_us": round(mean_us(rv_marks, "up_kv_len"), 2),
+        "kv_len_us": round(med_us(rv_marks, "up_kv_len"), 2),
         "graph_step_us": round(graph_step_us, 2),
         "fused_pipeline": fused_rec,
         "keep_ratio": round(kept / T, 5),
