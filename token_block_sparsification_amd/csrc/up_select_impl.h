@@ -44,7 +44,10 @@
 namespace up {
 namespace {
 
-constexpr int kSelectThreads = 256;
+#ifndef UP_SEL_THREADS
+#define UP_SEL_THREADS 512
+#endif
+constexpr int kSelectThreads = UP_SEL_THREADS;
 constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int64_t kMaxBlocksPerRequest = 1 << 24;
 constexpr int kStageMax = 4096;         // blocks staged in LDS
