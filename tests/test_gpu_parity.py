@@ -91,6 +91,18 @@ def test_wide_query_groups(hq, hkv, d, n):
     _end_to_end(W.make_inputs(w), n, 64, name=w.name)
 
 
+def test_long_chunk_boundaries():
+    """A packed batch large enough that the workgroup rule picks 4096-key
+    chunks: requests one key short of, exactly at and one key past chunk
+    edges, multi-chunk requests with ragged last chunks, and the causal tail
+    falling inside the last chunk of each."""
+    lengths = (4095, 4096, 4097, 8191, 12289, 30000, 70001)
+    w = W.Workload(name="long_chunks", lengths=lengths, hq=32, hkv=8, head_dim=128,
+                   hidden_dim=64, hidden_dtype="bf16", seed=6101, plant_frac=0.05,
+                   num_seqs=len(lengths))
+    _end_to_end(W.make_inputs(w), 128, 64, name=w.name)
+
+
 def test_tail_equals_n_and_small_p():
     w = W.Workload(name="p_sweep", lengths=(4096, 2000), hq=8, hkv=2, head_dim=128, hidden_dim=32,
                    hidden_dtype="bf16", seed=6001, plant_frac=0.1, num_seqs=2)
