@@ -239,7 +239,7 @@ def main():
         del src, dst
     torch.cuda.synchronize()
     kept = int(ws.cu_seqlens_out[-1].item())
-    dominant = max(("up_score", "up_compact"), key=lambda n: mean_us(warm_marks, n)) \
+    dominant = max(("up_score", "up_compact"), key=lambda n: med_us(warm_marks, n)) \
         if warm_marks else "up_compact"
 
     # Timed region: K steps; only the dominant call is bracketed by events

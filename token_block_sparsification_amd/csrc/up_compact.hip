@@ -21,7 +21,7 @@
 //     L2 on every publish and poll.  The last workgroup to finish (a done
 //     counter) clears the status words and both counters, so the next call
 //     starts from a clean workspace without a separate clearing launch.
-//   up_compact_copy_kernel   one workgroup per (block, 8 KiB piece): a kept
+//   up_compact_copy_kernel   one workgroup per (block, 4 KiB piece): a kept
 //     block is a run of G consecutive rows, copied as one flat byte range with
 //     16-byte non-temporal loads and stores; dropped rows are never read.
 // Splitting the gather from the scan lets the copy use small, uniform work
@@ -39,19 +39,25 @@ namespace {
 constexpr int kCompactThreads = 256;
 constexpr int kScanPerThread = 4;
 constexpr int kScanTileBlocks = kCompactThreads * kScanPerThread;  // blocks per scan tile
-// Copy work items: 8 KiB per 256-thread workgroup, one 16-byte vector in
+// Copy work items: 4 KiB per 128-thread workgroup, one 16-byte vector in
 // flight per lane (two rounds).  Many short-lived workgroups keep more HBM
-// requests in flight across the chip than fewer long ones: per up_compact call
-// at L = 131072, D = 4096 bf16, 8 KiB x 1 took 355 us against 377 us for
-// 32 KiB x 4 vectors (1458 vs 1663 us on a 16-request batch; 4 KiB: 366 us).
+// requests in flight across the chip than fewer long ones.  Per up_compact
+// call at L = 131072, D = 4096 bf16 (16-request batch in brackets): 128 x 4 KiB
+// 341 us (1376), 128 x 2 KiB 372, 128 x 4 KiB with both vectors in flight 352,
+// 64 x 4 KiB 348 (1421), 64 x 2 KiB 348 (1406), 256 x 8 KiB 358 (1462),
+// 256 x 32 KiB with four vectors in flight 377 (1663), 512 x 16 KiB 380 (1590).
 #ifndef UP_PIECE_KIB
-#define UP_PIECE_KIB 8
+#define UP_PIECE_KIB 4
 #endif
 #ifndef UP_COPY_UNROLL
 #define UP_COPY_UNROLL 1
 #endif
 constexpr int64_t kPieceBytes = (int64_t)UP_PIECE_KIB << 10;       // bytes per copy work item
 constexpr int64_t kRowPieceBytes = 32 << 10;  // per work item when rows are strided (a wave per row)
+#ifndef UP_COPY_THREADS
+#define UP_COPY_THREADS 128
+#endif
+constexpr int kCopyThreads = UP_COPY_THREADS;  // threads per copy workgroup
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
@@ -259,14 +265,14 @@ __device__ __forceinline__ void copy_flat(char* __restrict__ dst, const char* __
   V* d = reinterpret_cast<V*>(dst);
   const int64_t n = nbytes / VW;
   int64_t i = threadIdx.x;
-  for (; i + (U - 1) * kCompactThreads < n; i += U * kCompactThreads) {
+  for (; i + (U - 1) * kCopyThreads < n; i += U * kCopyThreads) {
     V r[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = __builtin_nontemporal_load(s + i + u * kCompactThreads);
+    for (int u = 0; u < U; ++u) r[u] = __builtin_nontemporal_load(s + i + u * kCopyThreads);
 #pragma unroll
-    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(r[u], d + i + u * kCompactThreads);
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(r[u], d + i + u * kCopyThreads);
   }
-  for (; i < n; i += kCompactThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
+  for (; i < n; i += kCopyThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
 }
 
 // Copy `rows` rows of row_bytes between row layouts with the given strides,
@@ -278,7 +284,7 @@ __device__ __forceinline__ void copy_rows(char* __restrict__ dst, int64_t dst_st
   typedef typename Vec<VW>::T V;
   const int64_t vpr = row_bytes / VW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = wave; r < rows; r += kCompactThreads / 64) {
+  for (int r = wave; r < rows; r += kCopyThreads / 64) {
     const V* s = reinterpret_cast<const V*>(src + (int64_t)r * src_stride);
     V* d = reinterpret_cast<V*>(dst + (int64_t)r * dst_stride);
     for (int64_t c = lane; c < vpr; c += 64) __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
@@ -292,7 +298,7 @@ __device__ __forceinline__ void copy_rows(char* __restrict__ dst, int64_t dst_st
 // rows (hidden_out side) go back to their own rows of the full buffer
 // (hidden side); positions are not touched.
 template <int VW, bool REVIVE>
-__global__ void __launch_bounds__(kCompactThreads) up_compact_copy_kernel(CompactArgs a) {
+__global__ void __launch_bounds__(kCopyThreads) up_compact_copy_kernel(CompactArgs a) {
   const int64_t items = a.num_blocks * a.pieces;
   for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
     int64_t b, piece;
@@ -335,7 +341,7 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_copy_kernel(Compac
       }
     }
     if (!REVIVE && a.positions && piece == 0)
-      for (int i = threadIdx.x; i < d.rows; i += kCompactThreads)
+      for (int i = threadIdx.x; i < d.rows; i += kCopyThreads)
         a.positions_out[d.dst + i] = a.positions[d.src + i];
   }
 }
@@ -666,16 +672,16 @@ struct GatherCall {
 template <bool REVIVE>
 void launch_copy(const up::CompactArgs& a, dim3 grid, uintptr_t al, hipStream_t stream) {
   if ((al & 15) == 0)
-    hipLaunchKernelGGL((up::up_compact_copy_kernel<16, REVIVE>), grid, dim3(up::kCompactThreads), 0,
+    hipLaunchKernelGGL((up::up_compact_copy_kernel<16, REVIVE>), grid, dim3(up::kCopyThreads), 0,
                        stream, a);
   else if ((al & 7) == 0)
-    hipLaunchKernelGGL((up::up_compact_copy_kernel<8, REVIVE>), grid, dim3(up::kCompactThreads), 0,
+    hipLaunchKernelGGL((up::up_compact_copy_kernel<8, REVIVE>), grid, dim3(up::kCopyThreads), 0,
                        stream, a);
   else if ((al & 3) == 0)
-    hipLaunchKernelGGL((up::up_compact_copy_kernel<4, REVIVE>), grid, dim3(up::kCompactThreads), 0,
+    hipLaunchKernelGGL((up::up_compact_copy_kernel<4, REVIVE>), grid, dim3(up::kCopyThreads), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((up::up_compact_copy_kernel<1, REVIVE>), grid, dim3(up::kCompactThreads), 0,
+    hipLaunchKernelGGL((up::up_compact_copy_kernel<1, REVIVE>), grid, dim3(up::kCopyThreads), 0,
                        stream, a);
 }
 
