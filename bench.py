@@ -85,6 +85,7 @@ def load_traffic(kernel: str, src: str, launches_per_call: int = 1):
 
 
 COPY_BYTES = 1 << 30
+EVENT_EVERY = 4  # timed steps per bracketed dominant call
 # name in traffic.json -> (source file, pattern of the dispatch names it covers)
 TRAFFIC_KERNELS = {
     "up_compact_copy_kernel": ("up_compact.hip", r"\bup_compact_copy_kernel<\d+, false>"),
@@ -223,13 +224,9 @@ def main():
     gc.collect()
     gc.disable()
 
-    # Warm-up; its last steps bracket every call to find the dominant one.
-    warm_marks = []
+    # Warm-up (untimed).
     for i in range(args.warmup):
-        m = new_marks(calls) if i >= args.warmup // 2 else None
-        step(layer=i, marks=m)
-        if m:
-            warm_marks.append(m)
+        step(layer=i)
         U.up_history_init(ledger, B, cap)
     if args.copy_probe:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
@@ -239,20 +236,25 @@ def main():
         del src, dst
     torch.cuda.synchronize()
     kept = int(ws.cu_seqlens_out[-1].item())
-    dominant = max(("up_score", "up_compact"), key=lambda n: med_us(warm_marks, n)) \
-        if warm_marks else "up_compact"
 
-    # Timed region: K steps; only the dominant call is bracketed by events
-    # (each event record costs a few microseconds of queue time).
+    # Timed region: K steps; on every EVENT_EVERY-th step the two large calls
+    # (up_score, up_compact) are bracketed by events, and the larger of them
+    # over the timed region is the dominant one.  Each event record leaves
+    # the GPU idle for ~5 us, so bracketing every step would add ~11 us per
+    # call bracketed.
     K = args.steps
-    timed_marks = [new_marks([dominant]) for _ in range(K)]
+    big = ("up_score", "up_compact")
+    sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
+    timed_marks = {i: new_marks(list(big)) for i in sampled}
     U.up_history_init(ledger, B, cap)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(layer=i, marks=timed_marks[i])
+        step(layer=i, marks=timed_marks.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    timed_marks = [timed_marks[i] for i in sampled]
+    dominant = max(big, key=lambda n: mean_us(timed_marks, n))
     dominant_us = mean_us(timed_marks, dominant)
     dom_all = [m[dominant][0].elapsed_time(m[dominant][1]) * 1e3 for m in timed_marks]
 
@@ -397,7 +399,8 @@ def main():
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
                     "traffic": traffic,
                     "algorithmic_bytes_per_launch": int(compact_bytes),
-                    "duration": "HIP events around up_compact (scan + copy launches)"}
+                    "duration": ("HIP events around up_compact (scan + copy launches) on every "
+                                 f"{EVENT_EVERY}th step of the timed region ({len(dom_all)} launches)")}
     else:
         roofline = {"kernel": "up_score (rowstats+combine+colsum+blockmean)", "bound": "mfma",
                     "achieved": round(score_tflops_exec, 1), "peak": PEAK_BF16_TFLOPS,
