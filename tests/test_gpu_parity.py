@@ -286,6 +286,50 @@ def test_compact_isolated(dtype, dim, strided):
         assert not ws.view(torch.int32)[:2].any() and not ws[256:256 + 8 * tiles].any()
 
 
+def test_compact_workspace_across_batch_sizes():
+    """One compaction workspace, sized for the largest batch, serves a
+    sequence of batches whose scans span 3, 1, 2 and again 3 tiles of 1024
+    blocks (a revival call in between): every call is bit-exact and leaves
+    the workspace clean for the next, whatever the previous call's size."""
+    dev = torch.device("cuda")
+    G = 16
+    gen = torch.Generator().manual_seed(4242)
+    shapes = [[20000, 7, 16001, 2500], [900, 0, 31], [17000, 100, 33], [20000, 7, 16001, 2500]]
+    T_max = max(sum(x) for x in shapes)
+    cu_max = torch.tensor(np.concatenate([[0], np.cumsum(shapes[0])]), dtype=torch.int32)
+    ws = U.new_compact_workspace(cu_max, G, dev)
+    for lens in shapes:
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+        batch = U.Batch.make(cu, G, dev)
+        T = batch.num_tokens
+        assert U.up_compact_workspace_size(cu, G) <= ws.numel()
+        hidden = torch.randint(-1000, 1000, (T, 24), generator=gen).to(torch.int16).to(dev)
+        pos = torch.randperm(T, generator=gen).to(torch.int32).to(dev)
+        mask_np = (torch.rand(batch.num_blocks, generator=gen) < 0.6).numpy().astype(np.uint8)
+        mask = torch.from_numpy(mask_np).to(dev)
+        out = torch.zeros((T_max, 24), dtype=torch.int16, device=dev)
+        pout = torch.full((T_max,), -1, dtype=torch.int32, device=dev)
+        cu_out = torch.empty(len(lens) + 1, dtype=torch.int32, device=dev)
+        U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, hidden,
+                     pos, out, pout, cu_out, ws)
+        full = torch.zeros_like(hidden)
+        U.up_revive(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, out, full,
+                    ws)
+        torch.cuda.synchronize()
+        keep = O.token_keep(mask_np, cu.numpy(), G)
+        idx = torch.from_numpy(np.flatnonzero(keep)).to(dev)
+        n = idx.numel()
+        assert torch.equal(out[:n], hidden.index_select(0, idx))
+        assert torch.equal(pout[:n], pos.index_select(0, idx))
+        assert (pout[n:] == -1).all() and not out[n:].any()
+        _, _, cu_ref = O.compact(mask_np, np.zeros((T, 1)), np.zeros(T), cu.numpy(), G)
+        assert list(cu_out.cpu().numpy()) == list(cu_ref)
+        kept_rows = torch.from_numpy(keep).to(dev)
+        assert torch.equal(full[kept_rows], hidden[kept_rows]) and not full[~kept_rows].any()
+        tiles = -(-batch.num_blocks // 1024)
+        assert not ws.view(torch.int32)[:2].any() and not ws[256:256 + 8 * tiles].any()
+
+
 def test_compact_all_empty_and_no_positions():
     dev = torch.device("cuda")
     cu = torch.tensor([0, 0, 0, 0], dtype=torch.int32)
