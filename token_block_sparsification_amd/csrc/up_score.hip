@@ -988,7 +988,7 @@ up_blockmean_select_kernel(ScoreArgs a, SelectArgs sa) {
 #define UP_TILE_A256 1, 4, true
 #endif
 #ifndef UP_TILE_B256
-#define UP_TILE_B256 1, 4, false
+#define UP_TILE_B256 1, 4, true
 #endif
 template <int NT_, int W_, bool PIPE_>
 struct TileCfg {
