@@ -212,7 +212,7 @@ up_status up_compact_workspace_init(void* workspace, size_t workspace_bytes, hip
  * and cu_seqlens_out (tiles are claimed in order from an atomic counter, so
  * every look-back ends; the last tile to finish restores the workspace's
  * control and status words for the next call), then a copy kernel moves
- * each kept block in 32 KiB pieces.
+ * each kept block in 4 KiB pieces (32 KiB of rows when rows are strided).
  */
 up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                      const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
