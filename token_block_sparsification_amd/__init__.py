@@ -351,22 +351,11 @@ class Batch:
 
     @staticmethod
     def make(cu_seqlens, block: int, device) -> "Batch":
-        """Host arrays, and their device copies.  On a GPU both go up in one
-        asynchronous copy from freshly pinned memory (a copy from pageable
-        memory would wait for the stream to drain), each at a 256-byte
-        aligned offset of one device buffer."""
+        """Host arrays and their device copies.  The copies are synchronous, so
+        the device arrays are ready for calls on any stream."""
         cu_h = _host_i32(cu_seqlens)
         cb_h, n = up_make_cu_blocks(cu_h, block)
-        dev = torch.device(device)
-        if dev.type != "cuda":
-            return Batch(cu_h, cu_h.to(dev), cb_h, cb_h.to(dev), block, n)
-        m = cu_h.numel()
-        pad = (m + 63) // 64 * 64
-        buf = torch.zeros(2 * pad, dtype=torch.int32, pin_memory=True)
-        buf[:m] = cu_h
-        buf[pad:pad + m] = cb_h
-        d = buf.to(dev, non_blocking=True)
-        return Batch(cu_h, d[:m], cb_h, d[pad:pad + m], block, n)
+        return Batch(cu_h, cu_h.to(device), cb_h, cb_h.to(device), block, n)
 
 
 @dataclass
