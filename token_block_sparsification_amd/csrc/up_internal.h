@@ -32,7 +32,8 @@ struct ScoreGeometry {
   int rows_per_wg;   // query rows one column-sum workgroup holds in registers
   int rg;            // column-sum row groups per KV head
   int rg_a;          // row-statistics row groups per KV head
-  int ck;            // keys per workgroup chunk
+  int ck;            // keys per row-statistics workgroup chunk (sets the partials layout)
+  int ck_b;          // keys per column-sum workgroup chunk
   int max_chunks;    // chunks of the longest request
   size_t off_partial, off_bias, off_colpart, off_arrive, bytes;
 };

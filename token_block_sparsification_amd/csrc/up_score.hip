@@ -22,6 +22,8 @@
 // No floating-point atomics anywhere: results are bitwise reproducible.
 #include <math.h>
 
+#include <algorithm>
+#include <cstdint>
 #include <type_traits>
 
 #include "up_internal.h"
@@ -1012,7 +1014,8 @@ int rows_per_wg_for(int d, bool pass_b) {
 int64_t grid_for(const ScoreArgs& a) { return ceil_div(a.num_groups, 8) * 8 * a.rg; }
 
 template <int D>
-up_status launch_passes(const ScoreArgs& b_args, int rg_a, hipStream_t st) {
+up_status launch_passes(const ScoreArgs& b_args, int rg_a, int ck_b, int64_t groups_b,
+                        hipStream_t st) {
   using TA = typename Tiling<D>::A;
   using TB = typename Tiling<D>::B;
   ScoreArgs aa = b_args;
@@ -1027,8 +1030,11 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, hipStream_t st) {
                      st, b_args);
   s = check_launch("up_rowstats_combine_kernel");
   if (s != UP_OK) return s;
+  ScoreArgs bb = b_args;  // the column-sum pass chunks the keys its own way
+  bb.ck = ck_b;
+  bb.num_groups = groups_b;
   hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE>),
-                     dim3((unsigned)grid_for(b_args)), dim3(64 * TB::W), 0, st, b_args);
+                     dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb);
   return check_launch("up_colsum_kernel");
 }
 
@@ -1063,6 +1069,9 @@ namespace {
 #ifndef UP_MIN_WGS
 #define UP_MIN_WGS 512
 #endif
+#ifndef UP_CK_OVERHEAD
+#define UP_CK_OVERHEAD 256
+#endif
 // Key chunk per workgroup: the largest power of two in [256, UP_CK_MAX] that
 // still gives >= UP_MIN_WGS workgroups for this batch.  512 is one resident
 // round on the 256 CUs of gfx950 (two row-statistics workgroups per CU, and
@@ -1080,6 +1089,33 @@ int choose_ck(int num_seqs, const int32_t* cu_h, int hkv, int rg) {
     ck >>= 1;
   }
   return ck;
+}
+
+// Column-sum chunk: whole rounds of workgroups.  The column-sum workgroups of
+// a batch all take about the same time per key, so a last round that only
+// part fills the chip costs as much as a full one: pick the chunk (a multiple
+// of 64 keys, at most UP_CK_MAX) that minimises rounds x (chunk + per-workgroup
+// overhead), where one round holds UP_MIN_WGS / (hkv * rg) chunks (two
+// workgroups per CU on 256 CUs for the row groups of one KV head).  Single
+// requests keep the chunk of the rule above; a 16-request batch of 542K
+// tokens gets 2944-key chunks in 6 rounds instead of 4096-key chunks in 5,
+// the last one part full (column sums 657 vs 698 us).  Past 4096 requests the
+// search is skipped.
+int choose_ck_rounds(int num_seqs, const int32_t* cu_h, int hkv, int rg, int fallback) {
+  if (num_seqs > 4096) return fallback;
+  const int64_t per_round = std::max<int64_t>(1, UP_MIN_WGS / ((int64_t)hkv * rg));
+  int best_ck = fallback;
+  int64_t best = INT64_MAX;
+  for (int ck = 256; ck <= UP_CK_MAX; ck += 64) {
+    int64_t nch = 0;
+    for (int r = 0; r < num_seqs; ++r) nch += up::ceil_div(cu_h[r + 1] - cu_h[r], ck);
+    const int64_t cost = up::ceil_div(nch, per_round) * (ck + UP_CK_OVERHEAD);
+    if (cost <= best) {  // ties: the longer chunk
+      best = cost;
+      best_ck = ck;
+    }
+  }
+  return best_ck;
 }
 
 struct Layout {
@@ -1102,6 +1138,7 @@ up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int h
     return up::set_error(UP_ERR_UNSUPPORTED, "n_query %d not in [1, 4096]", n_query);
   up::ScoreGeometry g = up::score_geometry(num_seqs, T, max_len, hq, hkv, head_dim, n_query);
   g.ck = choose_ck(num_seqs, cu_h, hkv, g.rg > g.rg_a ? g.rg : g.rg_a);
+  g.ck_b = choose_ck_rounds(num_seqs, cu_h, hkv, g.rg > g.rg_a ? g.rg : g.rg_a, g.ck);
   g.max_chunks = (int)(max_len > 0 ? up::ceil_div(max_len, g.ck) : 1);
   size_t off = 0;
   g.off_partial = off;
@@ -1231,14 +1268,18 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   a.kept = sel ? sel->kept_tokens : nullptr;
 
   a.num_groups = 0;
-  for (int r = 0; r < num_seqs; ++r)
+  int64_t groups_b = 0;
+  for (int r = 0; r < num_seqs; ++r) {
     a.num_groups += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], a.ck) * (int64_t)hkv;
-  const int64_t nwg = up::ceil_div(a.num_groups, 8) * 8 * (a.rg > lay.g.rg_a ? a.rg : lay.g.rg_a);
+    groups_b += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], lay.g.ck_b) * (int64_t)hkv;
+  }
+  const int64_t rgm = a.rg > lay.g.rg_a ? a.rg : lay.g.rg_a;
+  const int64_t nwg = up::ceil_div(std::max(a.num_groups, groups_b), 8) * 8 * rgm;
   if (nwg > 0x7fffffff) return up::set_error(UP_ERR_UNSUPPORTED, "grid too large");
   switch (head_dim) {
-    case 64: st = up::launch_passes<64>(a, lay.g.rg_a, stream); break;
-    case 128: st = up::launch_passes<128>(a, lay.g.rg_a, stream); break;
-    default: st = up::launch_passes<256>(a, lay.g.rg_a, stream); break;
+    case 64: st = up::launch_passes<64>(a, lay.g.rg_a, lay.g.ck_b, groups_b, stream); break;
+    case 128: st = up::launch_passes<128>(a, lay.g.rg_a, lay.g.ck_b, groups_b, stream); break;
+    default: st = up::launch_passes<256>(a, lay.g.rg_a, lay.g.ck_b, groups_b, stream); break;
   }
   if (st != UP_OK) return st;
   if (N > 0) {
