@@ -43,6 +43,11 @@ constexpr int kRing = 4;  // LDS tiles per ring: two resident + two in flight
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
+// Column-sum pass: walk its work groups last to first, so that its first
+// workgroups read the keys the row-statistics pass read last (still cached).
+#ifndef UP_REVERSE_B
+#define UP_REVERSE_B 1
+#endif
 struct ScoreArgs {
   const int32_t* cu_seqlens;
   const int32_t* cu_blocks;
@@ -52,6 +57,7 @@ struct ScoreArgs {
   int num_seqs, hq, hkv, rgqa, n_query, block;
   int ck, max_chunks, rg, rows_per_wg;
   int64_t num_groups;  // real (request, KV head, key chunk) groups
+  int reverse;         // walk the groups last to first
   float c;  // scale * log2(e)
   float2* partial;  // [B][hq][n_query][max_chunks] (raw max, sum of exp2)
   float* bias;      // [B][hkv][rgqa * n_query], row order of the KV group
@@ -100,6 +106,7 @@ __device__ __forceinline__ Work decode_work(const ScoreArgs& a) {
   wk.rgi = (int)(rem >> 3);
   int64_t q = blk * 8 + (rem & 7);
   wk.valid = q < a.num_groups;
+  if (a.reverse) q = a.num_groups - 1 - q;
   wk.req = 0;
   wk.g = 0;
   wk.chunk = 0;
@@ -1033,6 +1040,7 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, int ck_b, int64_t gro
   ScoreArgs bb = b_args;  // the column-sum pass chunks the keys its own way
   bb.ck = ck_b;
   bb.num_groups = groups_b;
+  bb.reverse = UP_REVERSE_B;
   hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE>),
                      dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb);
   return check_launch("up_colsum_kernel");
