@@ -148,7 +148,7 @@ def main():
         write_traffic(*args.write_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the path runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the head-parallel design is described, not built)", file=sys.stderr)
         sys.exit(2)
 
