@@ -39,7 +39,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // Keys per LDS tile: two 32-wide MFMA tiles, one for head_dim 256 so that a
 // four-tile ring stays at 64 KiB of LDS.
 template <int D> struct KeysPerTile { static constexpr int value = D >= 256 ? 32 : 64; };
-constexpr int kRing = 4;  // LDS tiles per ring: two resident + two in flight
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 
@@ -127,6 +126,37 @@ __device__ __forceinline__ Work decode_work(const ScoreArgs& a) {
   return wk;
 }
 
+// One 16-byte-per-lane global->LDS load (global_load_lds_dwordx4): lane i
+// writes its 16 bytes at LDS byte address lds + 16 i.  Issued from an asm
+// statement so that the compiler's wait-count pass does not track it: that
+// pass cannot tell which ring slot an LDS DMA writes, and otherwise makes the
+// next LDS read of any slot wait for every DMA in flight (vmcnt(0)), i.e. for
+// the prefetch just issued.  The kernels order the ring by hand instead: an
+// explicit s_waitcnt vmcnt(N) and a workgroup barrier precede every read of a
+// slot, and the last tiles wait for vmcnt(0) before the workgroup ends.  The
+// statement has no register outputs, so nothing the compiler allocates can be
+// overwritten by the load in flight.
+__device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // m0 (the LDS destination base) is saved and restored inside the
+  // statement: the compiler reserves m0 and may keep a value of its own there.
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
+#else
+  (void)src;
+  (void)lds;
+#endif
+}
+
 // Key rows of one LDS tile, fetched with direct global->LDS loads
 // (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at base + 16 i),
 // so no registers stage the tile.  Rows are D*2 bytes, unpadded; the 16-byte
@@ -152,8 +182,7 @@ struct KTile {
       const int r = j * RPI + lane / CHUNKS;
       const int c = (lane % CHUNKS) ^ (r & SWZ);
       const int key = min(tkey0 + r, key_end - 1);
-      __builtin_amdgcn_global_load_lds(kbase + (int64_t)key * k_tok + c * 8, lds + j * RPI * D, 16,
-                                       0, 0);
+      lds_dma16(kbase + (int64_t)key * k_tok + c * 8, lds + j * RPI * D);
     }
   }
   // Element offset of chunk c of tile row r.
@@ -193,18 +222,9 @@ struct KStream {
   // Tile t, known to hold KT keys below key1.
   __device__ __forceinline__ void fetch_full(int t, uint16_t* dst) const {
     const uint16_t* tb = kbase + (int64_t)(key0 + t * Tile::KT) * k_tok;
-    // Device pass only: the host pass never emits this body, and the
-    // target builtin in a member of a class template shared by two kernels
-    // otherwise invalidates the second kernel's host-side launch stub.
-#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int i = 0; i < Tile::INSTS; ++i)
-      __builtin_amdgcn_global_load_lds(tb + off[i], dst + (wave * Tile::INSTS + i) * Tile::RPI * D,
-                                       16, 0, 0);
-#else
-    (void)tb;
-    (void)dst;
-#endif
+      lds_dma16(tb + off[i], dst + (wave * Tile::INSTS + i) * Tile::RPI * D);
   }
   // Any tile t of the chunk.
   __device__ __forceinline__ void fetch(int t, uint16_t* dst) const {
@@ -213,7 +233,6 @@ struct KStream {
     else Tile::fetch(kbase, k_tok, tk, key1, dst, wave, lane);
   }
 };
-
 
 // Workgroup barrier that waits only for this wave's LDS operations; the K
 // tile fetches in flight are covered by an explicit wait_vmcnt before it.
@@ -235,26 +254,49 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename Stream>
+// The K ring has RING slots (an even number >= 4).  When iteration it starts,
+// tiles it and it+1 are resident and tiles it+2 .. it+RING-2 are in flight;
+// iteration it fetches tile it+RING-1 into the slot tile it-1 left, and ends
+// once tile it+2 has landed, so RING-3 tiles stay in flight behind the one
+// the next iteration needs.  Loads return in issue order, so waiting until at
+// most (RING-3) tiles' worth of loads are outstanding is enough (stores the
+// pass issues in between only make that wait longer, never shorter).
+template <int RING, typename Stream>
 __device__ __forceinline__ void ring_prologue(const Stream& ks, int ntiles,
                                               uint16_t (*kl)[Stream::Tile::ELEMS]) {
-  ks.fetch(0, kl[0]);
-  if (ntiles > 1) ks.fetch(1, kl[1]);
-  if (ntiles > 2) {
-    ks.fetch(2, kl[2]);
-    wait_vmcnt<Stream::Tile::INSTS>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  static_assert(RING >= 4 && RING % 2 == 0, "ring of an even number of slots, at least 4");
+#pragma unroll
+  for (int t = 0; t < RING - 1; ++t)
+    if (t < ntiles) ks.fetch(t, kl[t]);
+  if (ntiles >= RING - 1) wait_vmcnt<(RING - 3) * Stream::Tile::INSTS>();
+  else wait_vmcnt<0>();
   lds_barrier();
 }
 
 // End of one ring iteration: tile it+2 resident in LDS for every wave.
-// FETCHED = tile it+3 was fetched this iteration and may stay in flight.
-template <typename Tile, bool FETCHED>
+// FETCHED = tile it+RING-1 was fetched this iteration (so were the tiles
+// between it+3 and it), and RING-3 tiles may stay in flight.
+template <int RING, typename Tile, bool FETCHED>
 __device__ __forceinline__ void ring_step() {
-  if constexpr (FETCHED) wait_vmcnt<Tile::INSTS>(); else wait_vmcnt<0>();
+  if constexpr (FETCHED) wait_vmcnt<(RING - 3) * Tile::INSTS>(); else wait_vmcnt<0>();
   lds_barrier();
+}
+
+// Ring iterations unrolled per trip of the steady-state loop (even, so a
+// tile's parity is known at compile time).
+#ifndef UP_RING_UNROLL
+#define UP_RING_UNROLL 4
+#endif
+constexpr int kUnroll = UP_RING_UNROLL;
+static_assert(kUnroll >= 2 && kUnroll % 2 == 0, "even unroll");
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 
@@ -458,12 +500,12 @@ __device__ __forceinline__ void rowstats_iter(const uint16_t* cur, const uint16_
   }
 }
 
-template <int D, int NT, int W, bool PIPE>
+template <int D, int NT, int W, bool PIPE, int RING>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 up_rowstats_kernel(ScoreArgs a) {
   using Tile = KTile<D, W>;
   constexpr int KT = Tile::KT;
-  __shared__ __attribute__((aligned(16))) uint16_t kl[kRing][Tile::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t kl[RING][Tile::ELEMS];
 
   const Work wk = decode_work(a);
   if (!wk.valid) return;
@@ -498,9 +540,11 @@ up_rowstats_kernel(ScoreArgs a) {
   // leading tiles that need no mask: every key < key1 and <= every tail row
   const int lim = min(key1, qpos0 + 1);
   const int nfast = lim > key0 ? (lim - key0) / KT : 0;
+  bf16x8_t af[D / 16];
+  int it = 0;
   KStream<D, W> ks;
   ks.init(kbase, a.k_tok, key0, key1, wave, lane);
-  ring_prologue(ks, ntiles, kl);
+  ring_prologue<RING>(ks, ntiles, kl);
 
   // Mask-free tiles first (software-pipelined when PIPE), then the tiles
   // that meet the causal diagonal or the chunk's end, in straight order.
@@ -508,9 +552,7 @@ up_rowstats_kernel(ScoreArgs a) {
   // count, so its body stays one basic block the scheduler can interleave;
   // the last few iterations (no prefetch left or a ragged one) wait for all.
   const int nfull = (key1 - key0) / KT;
-  const int nmain = max(0, min(nfast, nfull - 3));
-  bf16x8_t af[D / 16];
-  int it = 0;
+  const int nmain = max(0, min(nfast, nfull - (RING - 1)));
   if (nfast > 0) {
     f32x16_t acc = {};
     if constexpr (PIPE) {
@@ -518,34 +560,32 @@ up_rowstats_kernel(ScoreArgs a) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) acc = mfma32(af[s], qf[0][s], acc);
     }
-    // Steady state unrolled over the ring, so every LDS slot address is a
-    // compile-time constant (it starts at 0, a multiple of kRing).
+    // Steady state unrolled over kUnroll tiles; with a ring of kUnroll slots
+    // every LDS slot address is a compile-time constant (it starts at 0).
     auto step = [&](auto u) {
       constexpr int U = decltype(u)::value;
-      ks.fetch_full(it + U + 3, kl[(U + 3) % kRing]);
-      rowstats_iter<D, NT, W, false, PIPE>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1,
-                                           lane, C, qf, ipos, m_run, l_run, acc, af);
-      ring_step<Tile, true>();
+      const int s0 = RING == kUnroll ? 0 : it % RING;
+      ks.fetch_full(it + U + RING - 1, kl[(s0 + U + RING - 1) % RING]);
+      rowstats_iter<D, NT, W, false, PIPE>(kl[(s0 + U) % RING], kl[(s0 + U + 1) % RING],
+                                           key0 + (it + U) * KT, key1, lane, C, qf, ipos, m_run,
+                                           l_run, acc, af);
+      ring_step<RING, Tile, true>();
     };
-    for (; it + kRing <= nmain; it += kRing) {
-      step(std::integral_constant<int, 0>{});
-      step(std::integral_constant<int, 1>{});
-      step(std::integral_constant<int, 2>{});
-      step(std::integral_constant<int, 3>{});
-    }
+    for (; it + kUnroll <= nmain; it += kUnroll) static_for<0, kUnroll>(step);
     for (; it < nfast; ++it) {
-      if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
-      rowstats_iter<D, NT, W, false, PIPE>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT,
+      const bool more = it + RING - 1 < ntiles;
+      if (more) ks.fetch(it + RING - 1, kl[(it + RING - 1) % RING]);
+      rowstats_iter<D, NT, W, false, PIPE>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT,
                                            key1, lane, C, qf, ipos, m_run, l_run, acc, af);
-      if (it + 3 < ntiles) ring_step<Tile, true>(); else ring_step<Tile, false>();
+      if (more) ring_step<RING, Tile, true>(); else ring_step<RING, Tile, false>();
     }
   }
   for (; it < ntiles; ++it) {
-    if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+    if (it + RING - 1 < ntiles) ks.fetch(it + RING - 1, kl[(it + RING - 1) % RING]);
     f32x16_t acc = {};
-    rowstats_iter<D, NT, W, true, false>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1,
+    rowstats_iter<D, NT, W, true, false>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT, key1,
                                          lane, C, qf, ipos, m_run, l_run, acc, af);
-    ring_step<Tile, false>();
+    ring_step<RING, Tile, false>();
   }
 
   // Merge the two half-waves (same row, disjoint keys) and write the partial.
@@ -751,12 +791,12 @@ __device__ __forceinline__ void colsum_flush(const float (*colrow)[64], int wave
   if (FULL || tkey0 + k < key1) colout[tkey0 + k] = sum;
 }
 
-template <int D, int NT, int W, bool PIPE>
+template <int D, int NT, int W, bool PIPE, int RING>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 up_colsum_kernel(ScoreArgs a) {
   using Tile = KTile<D, W>;
   constexpr int KT = Tile::KT;
-  __shared__ __attribute__((aligned(16))) uint16_t kl[kRing][Tile::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t kl[RING][Tile::ELEMS];
   __shared__ float colbuf[2][W][64];
 
   const Work wk = decode_work(a);
@@ -800,18 +840,18 @@ up_colsum_kernel(ScoreArgs a) {
   const int ntiles = (key1 - key0 + KT - 1) / KT;
   const int lim = min(key1, qpos0 + 1);
   const int nfast = lim > key0 ? (lim - key0) / KT : 0;
-  KStream<D, W> ks;
-  ks.init(kbase, a.k_tok, key0, key1, wave, lane);
-  ring_prologue(ks, ntiles, kl);
-
-  // Loop structure as in pass A: steady state with whole-tile prefetch and
-  // a fixed wait, then the last mask-free tiles, then the masked tiles.
-  const int nfull = (key1 - key0) / KT;
-  const int nmain = max(0, min(nfast, nfull - 3));
   constexpr bool DB = PIPE && (KT / 32) % 2 == 0;  // double-buffered fragments
   bf16x8_t kfb[DB ? 2 : 1][D / 16];
   auto& kf = kfb[0];
   int it = 0;
+  KStream<D, W> ks;
+  ks.init(kbase, a.k_tok, key0, key1, wave, lane);
+  ring_prologue<RING>(ks, ntiles, kl);
+
+  // Loop structure as in pass A: steady state with whole-tile prefetch and
+  // a fixed wait, then the last mask-free tiles, then the masked tiles.
+  const int nfull = (key1 - key0) / KT;
+  const int nmain = max(0, min(nfast, nfull - (RING - 1)));
   if (nfast > 0) {
     f32x16_t acc = {};
     if constexpr (PIPE) {
@@ -824,51 +864,49 @@ up_colsum_kernel(ScoreArgs a) {
     // hides the LDS reads (colbuf is double-buffered; the ring barrier at
     // the end of tile j+1 orders them before tile j+2 overwrites the buffer).
     auto step = [&](auto u) {
-      constexpr int U = decltype(u)::value;
-      ks.fetch_full(it + U + 3, kl[(U + 3) % kRing]);
+      constexpr int U = decltype(u)::value;  // it is a multiple of kUnroll (even): it+U has U's parity
+      const int s0 = RING == kUnroll ? 0 : it % RING;
+      ks.fetch_full(it + U + RING - 1, kl[(s0 + U + RING - 1) % RING]);
       if (it + U > 0)
         colsum_flush<W, KT, true>(colbuf[(U + 1) & 1], wave, lane, key0 + (it + U - 1) * KT, key1,
                                   colout);
       if constexpr (DB)
-        colsum_iter_db<D, NT, W>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1, lane,
-                                 wave, row0, R, n_eff, qpos0, C, qf, bv, colbuf[U & 1], acc, kfb);
+        colsum_iter_db<D, NT, W>(kl[(s0 + U) % RING], kl[(s0 + U + 1) % RING], key0 + (it + U) * KT,
+                                 key1, lane, wave, row0, R, n_eff, qpos0, C, qf, bv, colbuf[U & 1],
+                                 acc, kfb);
       else
-        colsum_iter<D, NT, W, false, PIPE>(kl[U], kl[(U + 1) % kRing], key0 + (it + U) * KT, key1,
-                                           lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
-                                           colbuf[U & 1], acc, kf);
-      ring_step<Tile, true>();
+        colsum_iter<D, NT, W, false, PIPE>(kl[(s0 + U) % RING], kl[(s0 + U + 1) % RING],
+                                           key0 + (it + U) * KT, key1, lane, wave, row0, R, n_eff,
+                                           qpos0, C, qf, bv, colbuf[U & 1], acc, kf);
+      ring_step<RING, Tile, true>();
     };
-    for (; it + kRing <= nmain; it += kRing) {
-      step(std::integral_constant<int, 0>{});
-      step(std::integral_constant<int, 1>{});
-      step(std::integral_constant<int, 2>{});
-      step(std::integral_constant<int, 3>{});
-    }
+    for (; it + kUnroll <= nmain; it += kUnroll) static_for<0, kUnroll>(step);
     for (; it < nfast; ++it) {
-      if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+      const bool more = it + RING - 1 < ntiles;
+      if (more) ks.fetch(it + RING - 1, kl[(it + RING - 1) % RING]);
       if (it > 0)
         colsum_flush<W, KT, false>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT, key1,
                                    colout);
       if constexpr (DB)
-        colsum_iter_db<D, NT, W>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1, lane,
+        colsum_iter_db<D, NT, W>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT, key1, lane,
                                  wave, row0, R, n_eff, qpos0, C, qf, bv, colbuf[it & 1], acc, kfb);
       else
-        colsum_iter<D, NT, W, false, PIPE>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT,
+        colsum_iter<D, NT, W, false, PIPE>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT,
                                            key1, lane, wave, row0, R, n_eff, qpos0, C, qf, bv,
                                            colbuf[it & 1], acc, kf);
-      if (it + 3 < ntiles) ring_step<Tile, true>(); else ring_step<Tile, false>();
+      if (more) ring_step<RING, Tile, true>(); else ring_step<RING, Tile, false>();
     }
   }
   for (; it < ntiles; ++it) {
-    if (it + 3 < ntiles) ks.fetch(it + 3, kl[(it + 3) % kRing]);
+    if (it + RING - 1 < ntiles) ks.fetch(it + RING - 1, kl[(it + RING - 1) % RING]);
     if (it > 0)
       colsum_flush<W, KT, false>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT, key1,
                                  colout);
     f32x16_t acc = {};
-    colsum_iter<D, NT, W, true, false>(kl[it % kRing], kl[(it + 1) % kRing], key0 + it * KT, key1,
+    colsum_iter<D, NT, W, true, false>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT, key1,
                                        lane, wave, row0, R, n_eff, qpos0, C, qf, bv, colbuf[it & 1],
                                        acc, kf);
-    ring_step<Tile, false>();
+    ring_step<RING, Tile, false>();
   }
   // the last tile (ntiles >= 1: the chunk holds at least one key)
   colsum_flush<W, KT, false>(colbuf[(ntiles - 1) & 1], wave, lane, key0 + (ntiles - 1) * KT, key1,
@@ -979,29 +1017,30 @@ up_blockmean_select_kernel(ScoreArgs a, SelectArgs sa) {
 }
 
 // Compile-time tiling per head_dim and pass: NT 32-row tiles per wave, W
-// waves per workgroup, PIPE = software-pipelined MFMA/VALU interleave.  Pass A
-// writes per-row partials, so the two passes may group rows differently.
+// waves per workgroup, PIPE = software-pipelined MFMA/VALU interleave, RING =
+// LDS slots of the K ring.  Pass A writes per-row partials, so the two passes
+// may group rows differently.
 #ifndef UP_TILE_A64
-#define UP_TILE_A64 2, 4, true
+#define UP_TILE_A64 2, 4, true, 4
 #endif
 #ifndef UP_TILE_B64
-#define UP_TILE_B64 2, 8, true
+#define UP_TILE_B64 2, 8, true, 4
 #endif
 #ifndef UP_TILE_A128
-#define UP_TILE_A128 2, 4, true
+#define UP_TILE_A128 2, 4, true, 4
 #endif
 #ifndef UP_TILE_B128
-#define UP_TILE_B128 2, 8, true
+#define UP_TILE_B128 2, 8, true, 4
 #endif
 #ifndef UP_TILE_A256
-#define UP_TILE_A256 1, 4, true
+#define UP_TILE_A256 1, 4, true, 4
 #endif
 #ifndef UP_TILE_B256
-#define UP_TILE_B256 1, 4, true
+#define UP_TILE_B256 1, 4, true, 4
 #endif
-template <int NT_, int W_, bool PIPE_>
+template <int NT_, int W_, bool PIPE_, int RING_>
 struct TileCfg {
-  static constexpr int NT = NT_, W = W_;
+  static constexpr int NT = NT_, W = W_, RING = RING_;
   static constexpr bool PIPE = PIPE_;
   static constexpr int ROWS = NT * 32 * W;
 };
@@ -1028,7 +1067,8 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, int ck_b, int64_t gro
   ScoreArgs aa = b_args;
   aa.rg = rg_a;
   aa.rows_per_wg = TA::ROWS;
-  hipLaunchKernelGGL((up_rowstats_kernel<D, TA::NT, TA::W, TA::PIPE>), dim3((unsigned)grid_for(aa)),
+  hipLaunchKernelGGL((up_rowstats_kernel<D, TA::NT, TA::W, TA::PIPE, TA::RING>),
+                     dim3((unsigned)grid_for(aa)),
                      dim3(64 * TA::W), 0, st, aa);
   up_status s = check_launch("up_rowstats_kernel");
   if (s != UP_OK) return s;
@@ -1041,7 +1081,7 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, int ck_b, int64_t gro
   bb.ck = ck_b;
   bb.num_groups = groups_b;
   bb.reverse = UP_REVERSE_B;
-  hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE>),
+  hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE, TB::RING>),
                      dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb);
   return check_launch("up_colsum_kernel");
 }
