@@ -59,6 +59,16 @@ MUTATIONS = {
     "trace_forced_mass_ignored": ("acc = float(sum(float(bs[b]) for b in range(len(bs)) if forced[b]))",
                                   "acc = 0.0"),
     "gather_add_sign": ("return round_to_format(h + d, fmt)", "return round_to_format(h - d, fmt)"),
+    "chain_sink_tail_swapped": ("mask, kept = select_topp(bsc, cu_seqlens, G, p, sink, tail)",
+                                "mask, kept = select_topp(bsc, cu_seqlens, G, p, tail, sink)"),
+    "chain_block_size_as_n": ("c = token_scores(q, k, cu_seqlens, n_query, scale)",
+                              "c = token_scores(q, k, cu_seqlens, G, scale)"),
+    "chain_n_as_block_size": ("bsc = block_scores(c, cu_seqlens, G)",
+                              "bsc = block_scores(c, cu_seqlens, n_query)"),
+    "chain_layer_id_ignored": ("history_append(ledger, layer_id, cu_out)",
+                               "history_append(ledger, 0, cu_out)"),
+    "chain_p_ignored": ("mask, kept = select_topp(bsc, cu_seqlens, G, p, sink, tail)",
+                        "mask, kept = select_topp(bsc, cu_seqlens, G, 0.99, sink, tail)"),
     "gather_add_delta_shifted": ("d = np.asarray(delta, dtype=np.float64)[: len(h)]",
                                  "d = np.asarray(delta, dtype=np.float64)[1: len(h) + 1]"),
 }

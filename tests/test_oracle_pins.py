@@ -409,6 +409,72 @@ def check_history():
     assert O.history_kv_len(led[2], 100, 99) == 16
 
 
+def check_chain_composition():
+    """run_chain is the composition of the pinned steps with its arguments in
+    their places: scores with n_query tail rows, block means over G, selection
+    with (p, sink, tail), compaction over G, one ledger entry per request
+    carrying layer_id.  The parameters are chosen pairwise distinct (n=40,
+    G=16, sink=32, tail=80, layer 9) so that a swapped or dropped argument
+    changes some output."""
+    lengths = [300, 17, 0, 129]
+    q, k, cu = _rand_qk(11, lengths, 6, 3, 8)
+    T = int(cu[-1])
+    rng = np.random.default_rng(12)
+    hidden = rng.integers(0, 2 ** 16, size=(T, 5), dtype=np.uint16)
+    pos = np.concatenate([np.arange(L) for L in lengths]).astype(np.int32)
+    n, G, p, sink, tail, layer = 40, 16, 0.8, 32, 80, 9
+    out = O.run_chain(q, k, hidden, pos, cu, n_query=n, G=G, p=p, sink=sink, tail=tail,
+                      layer_id=layer)
+    c = O.token_scores(q, k, cu, n)
+    bs = O.block_scores(c, cu, G)
+    mask, kept = O.select_topp(bs, cu, G, p, sink, tail)
+    h, po, cuo = O.compact(mask, hidden, pos, cu, G)
+    np.testing.assert_array_equal(out["token_scores"], c)
+    np.testing.assert_array_equal(out["block_scores"], bs)
+    np.testing.assert_array_equal(out["mask"], mask)
+    np.testing.assert_array_equal(out["kept"], kept)
+    np.testing.assert_array_equal(out["hidden_out"], h)
+    np.testing.assert_array_equal(out["positions_out"], po)
+    np.testing.assert_array_equal(out["cu_out"], cuo)
+    assert out["ledger"] == [[(layer, int(cuo[b + 1] - cuo[b]))] for b in range(len(lengths))]
+    assert 0 < int(cuo[-1]) < T      # the example really drops blocks
+
+
+def check_chain_hand_example():
+    """Whole path worked by hand.  Two requests, L = 8 and 3, one head, d = 1,
+    every key equal (so each tail row is uniform over the keys it sees),
+    n = 3, G = 2, p = 0.7, sink = 3, tail = 1, layer id 5.
+
+    Request 0: tail rows 5, 6, 7 see 6, 7, 8 keys, so in units of 1/168
+    c_0..c_5 = 28+24+21 = 73, c_6 = 24+21 = 45, c_7 = 21.  Blocks {0,1},
+    {2,3}, {4,5}, {6,7} score 73, 73, 73, 33; total 252, target 0.7*252 =
+    176.4.  Forced: blocks 0 and 1 (start below sink 3) and block 3 (overlaps
+    the last token), mass 179 >= 176.4, so block 2 is dropped: 6 tokens kept,
+    rows 0, 1, 2, 3, 6, 7.  (With sink and tail swapped blocks 0, 2, 3 would
+    be forced instead and block 1 dropped.)
+    Request 1 (shorter than n, all three rows are tail rows): c = 11/6, 5/6,
+    1/3; blocks {0,1}, {2} score 4/3, 1/3; both start below sink 3, so both
+    are kept: 3 tokens.
+    Ledger: (5, 6) and (5, 3); cu_seqlens_out = [0, 6, 9]."""
+    q = np.array([0.3, -1.0, 2.0, 0.5, 1.5, -0.7, 0.9, 1.1, 0.2, -0.4, 0.8]).reshape(11, 1, 1)
+    k = np.full((11, 1, 1), 0.6)
+    cu = [0, 8, 11]
+    hidden = np.arange(11, dtype=np.int64).reshape(11, 1) * 10
+    pos = np.array([0, 1, 2, 3, 4, 5, 6, 7, 0, 1, 2], dtype=np.int32)
+    out = O.run_chain(q, k, hidden, pos, cu, n_query=3, G=2, p=0.7, sink=3, tail=1, layer_id=5)
+    c0 = np.array([73, 73, 73, 73, 73, 73, 45, 21]) / 168.0
+    c1 = np.array([11 / 6, 5 / 6, 1 / 3])
+    np.testing.assert_allclose(out["token_scores"], np.concatenate([c0, c1]), rtol=1e-14)
+    np.testing.assert_allclose(out["block_scores"],
+                               [73 / 168, 73 / 168, 73 / 168, 33 / 168, 4 / 3, 1 / 3], rtol=1e-14)
+    np.testing.assert_array_equal(out["mask"], [1, 1, 0, 1, 1, 1])
+    np.testing.assert_array_equal(out["kept"], [6, 3])
+    np.testing.assert_array_equal(out["hidden_out"][:, 0], [0, 10, 20, 30, 60, 70, 80, 90, 100])
+    np.testing.assert_array_equal(out["positions_out"], [0, 1, 2, 3, 6, 7, 0, 1, 2])
+    np.testing.assert_array_equal(out["cu_out"], [0, 6, 9])
+    assert out["ledger"] == [[(5, 6)], [(5, 3)]]
+
+
 def check_widen_bf16():
     """bf16 widening agrees with torch's own bf16 -> fp64 conversion."""
     x = torch.randn(10000, dtype=torch.float64).to(torch.bfloat16)
@@ -542,7 +608,8 @@ ALL_CHECKS = [
     check_gqa_peak, check_head_additivity, check_n1_textbook_softmax, check_block_means,
     check_select_golden, check_one_hot, check_uniform_ceil, check_select_invariants,
     check_brute_force, check_scale_invariance, check_concentration, check_short_requests,
-    check_compaction, check_revival, check_history, check_widen_bf16, check_knife_edge_band,
+    check_compaction, check_revival, check_history, check_chain_composition,
+    check_chain_hand_example, check_widen_bf16, check_knife_edge_band,
     check_round_to_format,
     check_rmsnorm, check_compact_rmsnorm, check_gather_add,
 ]
