@@ -11,6 +11,7 @@
  *   up_score        tail-query importance scores, per-token and per-block
  *   up_select_topp  Top-p block mask with forced sink / tail blocks
  *   up_compact      gather of the kept rows + positions, new cu_seqlens
+ *                   (up_compact_status: its workspace's status bits)
  *   up_drop_history append (layer id, kept tokens) to each request's ledger
  * and, around it,
  *   up_kv_len       per-layer KV length read back from the ledger
@@ -178,7 +179,18 @@ up_status up_select_topp(int num_seqs, const int32_t* cu_seqlens_h, const int32_
 /* ------------------------------------------------------------------------ */
 
 /* Workspace bytes up_compact needs for this batch (control and status words,
- * one 16-byte copy descriptor per block). */
+ * one 16-byte copy descriptor per block).
+ *
+ * The first 256 bytes of a compaction workspace are its control block, uint32
+ * words:
+ *   [0] scan tile ticket and [1] done counter (zero between calls);
+ *   [2] status bits, sticky until read by up_compact_status (bit 0: a
+ *       look-back gave up waiting for a predecessor tile, so that call's
+ *       cu_seqlens_out and copy offsets are wrong; the copies stay within
+ *       out_capacity_rows);
+ *   [3] look-back poll limit: polls of one predecessor's status word before
+ *       giving up; 0 (what up_compact_workspace_init leaves) selects 2^24.
+ * The rest is per-tile scan state and the copy descriptors. */
 up_status up_compact_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int block,
                                     size_t* bytes);
 
@@ -210,9 +222,11 @@ up_status up_compact_workspace_init(void* workspace, size_t workspace_bytes, hip
  * Two kernel launches: a single-pass decoupled look-back scan (Merrill &
  * Garland 2016) over tiles of 1024 blocks writes each block's output row
  * and cu_seqlens_out (tiles are claimed in order from an atomic counter, so
- * every look-back ends; the last tile to finish restores the workspace's
- * control and status words for the next call), then a copy kernel moves
- * each kept block in 4 KiB pieces (32 KiB of rows when rows are strided).
+ * every predecessor a tile waits on has started; a wait that still exceeds
+ * the poll limit gives up and sets status bit 0, read with
+ * up_compact_status; the last tile to finish restores the workspace's
+ * counters and tile state for the next call), then a copy kernel moves each
+ * kept block in 4 KiB pieces (32 KiB of rows when rows are strided).
  */
 up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                      const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
@@ -221,6 +235,19 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
                      void* hidden_out, int32_t* positions_out, int32_t* cu_seqlens_out,
                      int64_t out_capacity_rows, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/*
+ * up_compact_status — the status bits of a compaction workspace (control word
+ * 2: bit 0 = a look-back gave up, see up_compact_workspace_size) as left by
+ * the calls enqueued before it on `stream` (up_compact, up_revive and the
+ * fused row operations share the scan).  The page requires the metadata
+ * update to be exact (§三), so a caller that must be sure checks this word.
+ * status   device int32 [1] (written).
+ * clear    nonzero: also clear the bits (the word keeps accumulating
+ *          otherwise).
+ */
+up_status up_compact_status(void* workspace, size_t workspace_bytes, int32_t* status, int clear,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Step 5 (cont.): drop-history ledger (§三)                                  */

@@ -204,3 +204,15 @@ def test_score_select_rejects_bad_arguments():
         a[i] = v
         st = lib.up_score_select(*a)
         assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())
+
+
+def test_compact_status_rejects_bad_arguments():
+    """Null pointers, a misaligned or too small workspace are rejected on the
+    host (nothing is dereferenced or enqueued)."""
+    lib = U.lib()
+    dummy = ctypes.c_void_p(1 << 20)
+    assert lib.up_compact_status(None, 4096, dummy, 1, None) == 1
+    assert lib.up_compact_status(dummy, 4096, None, 1, None) == 1
+    assert lib.up_compact_status(ctypes.c_void_p((1 << 20) + 16), 4096, dummy, 1, None) == 1
+    assert "aligned" in U.up_last_error()
+    assert lib.up_compact_status(dummy, 128, dummy, 1, None) == 3

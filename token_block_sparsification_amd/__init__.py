@@ -22,7 +22,7 @@ __all__ = [
     "UniprefillError", "lib", "LIB_PATH",
     "up_abi_version", "up_last_error", "up_make_cu_blocks",
     "up_score_workspace_size", "up_score", "up_select_topp",
-    "up_compact_workspace_size", "up_compact_workspace_init", "up_compact",
+    "up_compact_workspace_size", "up_compact_workspace_init", "up_compact", "up_compact_status",
     "up_history_bytes", "up_history_init", "up_drop_history", "up_kv_len", "up_revive",
     "up_compact_rmsnorm", "up_gather_add", "up_score_select",
     "Batch", "Workspace", "run_chain",
@@ -65,6 +65,7 @@ _SIGNATURES = {
     "up_compact_workspace_init": (_I, [_P, _SZ, _P]),
     "up_compact": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _SZ,
                         _P]),
+    "up_compact_status": (_I, [_P, _SZ, _P, _I, _P]),
     "up_history_bytes": (_SZ, [_I, _I]),
     "up_history_init": (_I, [_P, _I, _I, _P]),
     "up_drop_history": (_I, [_P, _I, _I, _I, _P, _P]),
@@ -240,6 +241,14 @@ def up_compact(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, 
                           hidden_out.shape[0], _ptr(workspace), workspace.numel(),
                           _stream(stream, hidden_out.device))
     _check("up_compact", st)
+
+
+def up_compact_status(workspace, status, clear: bool = True, stream=None) -> None:
+    """Copy the compaction workspace's status bits (bit 0: a look-back gave
+    up) into the device int32 tensor `status`, clearing them if `clear`."""
+    _check("up_compact_status", lib().up_compact_status(_ptr(workspace), workspace.numel(),
+                                                        _ptr(status), 1 if clear else 0,
+                                                        _stream(stream, workspace.device)))
 
 
 def up_history_init(ledger, num_seqs: int, capacity: int, stream=None) -> None:

@@ -61,7 +61,11 @@ constexpr int kCopyThreads = UP_COPY_THREADS;  // threads per copy workgroup
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
-constexpr int kSpinLimit = 1 << 24;
+// Polls of one predecessor's status word before a look-back gives up (when
+// control word 3 is 0).  Tiles are claimed in ticket order, so every
+// predecessor has started and publishes within a few microseconds; the
+// limit only bounds the wait if one never does.
+constexpr uint32_t kSpinLimit = 1u << 24;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -85,7 +89,7 @@ struct CompactArgs {
   int32_t* positions_out;
   int32_t* cu_out;    // NULL: not written (revival)
   uint64_t* flags;    // [num_tiles] scan tile status words
-  uint32_t* ctl;      // [0] tile ticket, [1] done counter, [2] sticky look-back timeout flag
+  uint32_t* ctl;      // [0] tile ticket, [1] done counter, [2] status bits, [3] poll limit
   BlockCopy* desc;    // [num_blocks]
   int64_t row_bytes, row_stride, capacity, num_blocks, num_tiles;
   int64_t pieces;      // copy work items per block
@@ -94,10 +98,21 @@ struct CompactArgs {
   int num_seqs, block;
 };
 
+// Status bit of control word 2: a look-back gave up on a predecessor tile.
+constexpr uint32_t kStatusLookbackGaveUp = 1u;
+
 // Zero a whole compaction workspace (control words and tile status words).
 __global__ void up_compact_init_kernel(uint32_t* ws, int64_t nwords) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nwords) ws[i] = 0;
+}
+
+// Copy the status bits of a compaction workspace, optionally clearing them.
+__global__ void up_compact_status_kernel(uint32_t* ctl, int32_t* out, int clear) {
+  if (threadIdx.x == 0) {
+    out[0] = (int32_t)ctl[2];
+    if (clear) ctl[2] = 0;
+  }
 }
 
 // Request owning block b: the last r with cu_blocks[r] <= b.
@@ -120,6 +135,7 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
   if (tid == 0) s_tile = (int64_t)atomicAdd(&a.ctl[0], 1u);
   __syncthreads();
   const int64_t t = s_tile;
+  const uint32_t poll_limit = a.ctl[3] ? a.ctl[3] : kSpinLimit;
 
   if (t == 0 && tid == 0 && a.cu_out) {
     // Output packing starts at 0; requests with no blocks before the first
@@ -184,13 +200,15 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
             int spins = 0;
             for (;;) {
               f = __hip_atomic_load(&a.flags[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              if ((f >> 62) != 0 || ++spins >= kSpinLimit) break;
+              if ((f >> 62) != 0 || (uint32_t)++spins >= poll_limit) break;
               __builtin_amdgcn_s_sleep(1);
             }
           }
           const uint64_t incl_lanes = __ballot((f >> 62) == 2);
           const int stop = incl_lanes ? __ffsll((unsigned long long)incl_lanes) - 1 : 63;
-          if (lane <= stop && (f >> 62) == 0) atomicOr(&a.ctl[2], 1u);  // predecessor never published
+          // a predecessor that never published counts as 0 rows: the
+          // offsets are wrong, so the call's status records it
+          if (lane <= stop && (f >> 62) == 0) atomicOr(&a.ctl[2], kStatusLookbackGaveUp);
           int64_t v = (lane <= stop) ? (int64_t)(f & kValueMask) : 0;
 #pragma unroll
           for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -229,9 +247,11 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
     }
   }
 
-  // Done counter: the last workgroup leaves the status words and counters
-  // zeroed for the next call (every other workgroup has finished its
-  // look-back before it counted itself done).
+  // Done counter: the last workgroup leaves the tile status words and the
+  // two counters zeroed for the next call (every other workgroup has
+  // finished its look-back before it counted itself done).  The status bits
+  // (word 2) stay until up_compact_status reads and clears them, and the
+  // poll limit (word 3) is the caller's setting.
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&a.ctl[1], 1u, __ATOMIC_RELAXED,
@@ -845,6 +865,19 @@ up_status up_compact_workspace_init(void* workspace, size_t workspace_bytes, hip
   hipLaunchKernelGGL(up::up_compact_init_kernel, dim3((unsigned)up::ceil_div(nwords, 256)), dim3(256),
                      0, stream, static_cast<uint32_t*>(workspace), nwords);
   return up::check_launch("up_compact_init_kernel");
+}
+
+up_status up_compact_status(void* workspace, size_t workspace_bytes, int32_t* status, int clear,
+                            hipStream_t stream) {
+  up::clear_error();
+  if (!workspace || !status) return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if ((uintptr_t)workspace & 255) return up::set_error(UP_ERR_INVALID, "workspace not 256-byte aligned");
+  if (workspace_bytes < 256) return up::set_error(UP_ERR_WORKSPACE, "workspace smaller than 256 bytes");
+  up_status st = up::check_device();
+  if (st != UP_OK) return st;
+  hipLaunchKernelGGL(up::up_compact_status_kernel, dim3(1), dim3(64), 0, stream,
+                     static_cast<uint32_t*>(workspace), status, clear ? 1 : 0);
+  return up::check_launch("up_compact_status_kernel");
 }
 
 up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
