@@ -189,7 +189,10 @@ up_status up_select_topp(int num_seqs, const int32_t* cu_seqlens_h, const int32_
  *       cu_seqlens_out and copy offsets are wrong; the copies stay within
  *       out_capacity_rows);
  *   [3] look-back poll limit: polls of one predecessor's status word before
- *       giving up; 0 (what up_compact_workspace_init leaves) selects 2^24.
+ *       giving up; 0 (what up_compact_workspace_init leaves) selects 2^24;
+ *   [4] call epoch, advanced by every call (a tile's status word counts only
+ *       with the current epoch, so nothing an earlier call left behind, for
+ *       any batch size, is taken for this call's).
  * The rest is per-tile scan state and the copy descriptors. */
 up_status up_compact_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, int block,
                                     size_t* bytes);
@@ -197,8 +200,9 @@ up_status up_compact_workspace_size(int num_seqs, const int32_t* cu_seqlens_h, i
 /*
  * Prepare a compaction workspace once, before its first up_compact call
  * (zeroes workspace_bytes bytes on `stream`).  Every up_compact call leaves
- * the workspace in this state again when it completes, so one workspace
- * serves any number of calls and any batch it is large enough for.
+ * the workspace prepared again when it completes (counters zero, epoch
+ * advanced), so one workspace serves any number of calls and any batch it is
+ * large enough for, in any order of sizes.
  * workspace: 256-byte aligned, >= 256 bytes.
  */
 up_status up_compact_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -259,3 +259,37 @@ def test_compact_lookback_give_up_is_reported():
     assert cu_out.cpu().tolist() == list(exp_cu)
     assert np.array_equal(h_out[:n].cpu().numpy(), exp_h)
     assert np.array_equal(p_out[:n].cpu().numpy(), exp_p)
+
+
+def test_compact_workspace_reuse_across_tile_counts():
+    """One workspace, batches of 4, then 40, then 4 scan tiles: the 40-tile
+    call's status words lie where the 4-tile call wrote copy descriptors, and
+    every call must still be exact (regression: stale descriptor bytes were
+    once read as published prefixes)."""
+    G = 16
+    ws = None
+    for nb, seed in ((4 * 1024 - 100, 1), (40 * 1024 - 7, 2), (4 * 1024 - 100, 3)):
+        L = nb * G
+        cu = torch.tensor([0, L - 5, L], dtype=torch.int32)
+        batch = U.Batch.make(cu, G, DEV)
+        if ws is None:
+            ws = U.new_compact_workspace(torch.tensor([0, 40 * 1024 * G], dtype=torch.int32), G, DEV)
+        gen = torch.Generator().manual_seed(seed)
+        hidden = torch.randint(-2 ** 30, 2 ** 30, (L, 1), dtype=torch.int32, generator=gen).to(DEV)
+        pos = torch.arange(L, dtype=torch.int32, device=DEV)
+        mask = (torch.rand(batch.num_blocks, generator=gen) < 0.5).to(torch.uint8).to(DEV)
+        h_out = torch.zeros_like(hidden)
+        p_out = torch.zeros_like(pos)
+        cu_out = torch.zeros(3, dtype=torch.int32, device=DEV)
+        status = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, hidden,
+                     pos, h_out, p_out, cu_out, ws)
+        U.up_compact_status(ws, status)
+        torch.cuda.synchronize()
+        exp_h, exp_p, exp_cu = O.compact(mask.cpu().numpy(), hidden.cpu().numpy(),
+                                         pos.cpu().numpy(), cu.tolist(), G)
+        n = int(exp_cu[-1])
+        assert cu_out.cpu().tolist() == list(exp_cu), nb
+        assert np.array_equal(h_out[:n].cpu().numpy(), exp_h), nb
+        assert np.array_equal(p_out[:n].cpu().numpy(), exp_p), nb
+        assert int(status[0]) == 0, nb

@@ -58,9 +58,19 @@ constexpr int64_t kRowPieceBytes = 32 << 10;  // per work item when rows are str
 #define UP_COPY_THREADS 128
 #endif
 constexpr int kCopyThreads = UP_COPY_THREADS;  // threads per copy workgroup
+// Tile status word: state in bits 63..62 (1 = aggregate, 2 = inclusive
+// prefix), the call's epoch in bits 61..31, the count in bits 30..0 (counts
+// are at most T < 2^31).  A word counts as published only with a state of 1
+// or 2 and this call's epoch, so nothing left in the status-word region by
+// earlier calls reads as published: their status words carry an older epoch,
+// and copy descriptors that a call with fewer tiles wrote there decode to
+// state 0 or 3 (their upper halves are a row count, a non-negative row or
+// -1).
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagIncl = 2ull << 62;
-constexpr uint64_t kValueMask = (1ull << 62) - 1;
+constexpr int kEpochShift = 31;
+constexpr uint64_t kEpochMask = (1ull << 31) - 1;
+constexpr uint64_t kValueMask = (1ull << 31) - 1;
 // Polls of one predecessor's status word before a look-back gives up (when
 // control word 3 is 0).  Tiles are claimed in ticket order, so every
 // predecessor has started and publishes within a few microseconds; the
@@ -89,7 +99,7 @@ struct CompactArgs {
   int32_t* positions_out;
   int32_t* cu_out;    // NULL: not written (revival)
   uint64_t* flags;    // [num_tiles] scan tile status words
-  uint32_t* ctl;      // [0] tile ticket, [1] done counter, [2] status bits, [3] poll limit
+  uint32_t* ctl;      // [0] tile ticket, [1] done counter, [2] status bits, [3] poll limit, [4] epoch
   BlockCopy* desc;    // [num_blocks]
   int64_t row_bytes, row_stride, capacity, num_blocks, num_tiles;
   int64_t pieces;      // copy work items per block
@@ -136,6 +146,10 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
   __syncthreads();
   const int64_t t = s_tile;
   const uint32_t poll_limit = a.ctl[3] ? a.ctl[3] : kSpinLimit;
+  // This call's epoch: the last workgroup advances it only after every
+  // workgroup of the call has counted itself done, so all read one value.
+  const uint64_t epoch = a.ctl[4] & kEpochMask;
+  const uint64_t tag = epoch << kEpochShift;
 
   if (t == 0 && tid == 0 && a.cu_out) {
     // Output packing starts at 0; requests with no blocks before the first
@@ -188,28 +202,31 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
       // predecessors per round trip: lane i reads tile (hi - i); the nearest
       // tile that already has an inclusive prefix ends the walk.
       if (lane == 0)
-        __hip_atomic_store(&a.flags[t], (t == 0 ? kFlagIncl : kFlagAgg) | (uint64_t)agg,
+        __hip_atomic_store(&a.flags[t], (t == 0 ? kFlagIncl : kFlagAgg) | tag | (uint64_t)agg,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       int64_t excl = 0;
       if (t > 0) {
         int64_t hi = t - 1;
         for (;;) {
           const int64_t p = hi - lane;
-          uint64_t f = kFlagIncl;  // before tile 0: an inclusive prefix of 0
+          uint64_t f = kFlagIncl | tag;  // before tile 0: an inclusive prefix of 0
+          uint32_t state = 2;
           if (p >= 0) {
             int spins = 0;
             for (;;) {
               f = __hip_atomic_load(&a.flags[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              if ((f >> 62) != 0 || (uint32_t)++spins >= poll_limit) break;
+              state = (uint32_t)(f >> 62);
+              if (state == 3 || ((f >> kEpochShift) & kEpochMask) != epoch) state = 0;
+              if (state != 0 || (uint32_t)++spins >= poll_limit) break;
               __builtin_amdgcn_s_sleep(1);
             }
           }
-          const uint64_t incl_lanes = __ballot((f >> 62) == 2);
+          const uint64_t incl_lanes = __ballot(state == 2);
           const int stop = incl_lanes ? __ffsll((unsigned long long)incl_lanes) - 1 : 63;
           // a predecessor that never published counts as 0 rows: the
           // offsets are wrong, so the call's status records it
-          if (lane <= stop && (f >> 62) == 0) atomicOr(&a.ctl[2], kStatusLookbackGaveUp);
-          int64_t v = (lane <= stop) ? (int64_t)(f & kValueMask) : 0;
+          if (lane <= stop && state == 0) atomicOr(&a.ctl[2], kStatusLookbackGaveUp);
+          int64_t v = (lane <= stop && state != 0) ? (int64_t)(f & kValueMask) : 0;
 #pragma unroll
           for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
           excl += v;
@@ -217,8 +234,8 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
           hi -= 64;
         }
         if (lane == 0)
-          __hip_atomic_store(&a.flags[t], kFlagIncl | (uint64_t)(excl + agg), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&a.flags[t], kFlagIncl | tag | (uint64_t)(excl + agg),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (lane == 0) s_excl = excl;
     }
@@ -248,10 +265,10 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
   }
 
   // Done counter: the last workgroup leaves the tile status words and the
-  // two counters zeroed for the next call (every other workgroup has
-  // finished its look-back before it counted itself done).  The status bits
-  // (word 2) stay until up_compact_status reads and clears them, and the
-  // poll limit (word 3) is the caller's setting.
+  // two counters zeroed and advances the epoch for the next call (every
+  // other workgroup has finished its look-back before it counted itself
+  // done).  The status bits (word 2) stay until up_compact_status reads and
+  // clears them, and the poll limit (word 3) is the caller's setting.
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&a.ctl[1], 1u, __ATOMIC_RELAXED,
@@ -264,6 +281,7 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
     if (tid == 0) {
       a.ctl[0] = 0;
       a.ctl[1] = 0;
+      a.ctl[4] = (uint32_t)((epoch + 1) & kEpochMask);
     }
   }
 }
