@@ -241,6 +241,30 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
                      hipStream_t stream);
 
 /*
+ * up_compact_noalloc — up_compact without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, outputs
+ * and kernels as up_compact, except:
+ * - the scan's control block, tile status words and copy descriptors live in
+ *   a device array inside the library (about 8 MiB, held by every GPU the
+ *   library runs on until the process ends); the call allocates nothing;
+ * - at most 2^19 blocks per call (UP_ERR_CAPACITY beyond that);
+ * - every call on one GPU shares that array, so calls that overlap on one GPU
+ *   (different streams without ordering) race; order them;
+ * - status   device int32 [1] or NULL: receives the array's status bits
+ *            accumulated since the last call that passed one (bit 0: a
+ *            look-back gave up, as for up_compact_status) and clears them.
+ * The first call on a device looks up the array's device address and clears
+ * its control words with a kernel on `stream`.
+ */
+up_status up_compact_noalloc(int num_seqs, const int32_t* cu_seqlens_h,
+                             const int32_t* cu_seqlens_d, const int32_t* cu_blocks_d, int block,
+                             const uint8_t* block_mask, const void* hidden, int64_t row_bytes,
+                             int64_t row_stride_bytes, const int32_t* positions, void* hidden_out,
+                             int32_t* positions_out, int32_t* cu_seqlens_out,
+                             int64_t out_capacity_rows, int32_t* status, hipStream_t stream);
+
+/*
  * up_compact_status — the status bits of a compaction workspace (control word
  * 2: bit 0 = a look-back gave up, see up_compact_workspace_size) as left by
  * the calls enqueued before it on `stream` (up_compact, up_revive and the

@@ -23,6 +23,7 @@ __all__ = [
     "up_abi_version", "up_last_error", "up_make_cu_blocks",
     "up_score_workspace_size", "up_score", "up_select_topp",
     "up_compact_workspace_size", "up_compact_workspace_init", "up_compact", "up_compact_status",
+    "up_compact_noalloc",
     "up_history_bytes", "up_history_init", "up_drop_history", "up_kv_len", "up_revive",
     "up_compact_rmsnorm", "up_gather_add", "up_score_select",
     "Batch", "Workspace", "run_chain",
@@ -66,6 +67,8 @@ _SIGNATURES = {
     "up_compact": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _SZ,
                         _P]),
     "up_compact_status": (_I, [_P, _SZ, _P, _I, _P]),
+    "up_compact_noalloc": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P,
+                                _P]),
     "up_history_bytes": (_SZ, [_I, _I]),
     "up_history_init": (_I, [_P, _I, _I, _P]),
     "up_drop_history": (_I, [_P, _I, _I, _I, _P, _P]),
@@ -241,6 +244,27 @@ def up_compact(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, 
                           hidden_out.shape[0], _ptr(workspace), workspace.numel(),
                           _stream(stream, hidden_out.device))
     _check("up_compact", st)
+
+
+def up_compact_noalloc(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, hidden,
+                       positions, hidden_out, positions_out, cu_seqlens_out, status=None,
+                       stream=None) -> None:
+    """up_compact with the library's own device scratch instead of a caller
+    workspace (for callers that cannot allocate); `status` (device int32 [1]
+    or None) receives and clears the scratch's status bits."""
+    if hidden.dim() < 1 or (hidden.dim() > 1 and not hidden[0].is_contiguous()):
+        raise ValueError("hidden rows must be contiguous")
+    if hidden_out.dtype != hidden.dtype:
+        raise ValueError("hidden_out must have hidden's dtype")
+    cu = _host_i32(cu_seqlens_h)
+    row_bytes = (hidden[0].numel() if hidden.dim() > 1 else 1) * hidden.element_size()
+    row_stride = hidden.stride(0) * hidden.element_size()
+    st = lib().up_compact_noalloc(cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_d), _ptr(cu_blocks_d),
+                                  block, _ptr(block_mask), _ptr(hidden), row_bytes, row_stride,
+                                  _ptr(positions), _ptr(hidden_out), _ptr(positions_out),
+                                  _ptr(cu_seqlens_out), hidden_out.shape[0], _ptr(status),
+                                  _stream(stream, hidden_out.device))
+    _check("up_compact_noalloc", st)
 
 
 def up_compact_status(workspace, status, clear: bool = True, stream=None) -> None:

@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "up_internal.h"
 
@@ -855,6 +856,51 @@ up_status check_rows(up_dtype dt, int64_t hidden_dim, std::initializer_list<int6
   return UP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free compaction: the workspace lives in a file-scope device
+// array instead of caller memory.  Each GPU the library runs on holds one
+// copy of it until the process ends; its device address is looked up once
+// per device (the array's name is a host-side stand-in, not a device
+// address), and every up_compact_noalloc call on that GPU shares it.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchMaxBlocks = int64_t(1) << 19;  // blocks per call (33.5M tokens at G = 64)
+constexpr size_t kScratchBytes =
+    256 + ((size_t)(kScratchMaxBlocks / up::kScanTileBlocks) * sizeof(uint64_t) + 255) / 256 * 256 +
+    (size_t)kScratchMaxBlocks * sizeof(up::BlockCopy);
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];      // device address of `scratch` per device (null: not looked up)
+std::mutex g_scratch_mu;
+
+// Device address of this device's copy of `scratch`; on the first call on a
+// device its control block and tile status words are cleared on `stream`
+// (a kernel, ahead of the call's own kernels on the same stream).
+up_status scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return up::set_error(UP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return up::set_error(UP_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return up::set_error(UP_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const int64_t nwords =
+        (int64_t)(256 + (kScratchMaxBlocks / up::kScanTileBlocks) * sizeof(uint64_t)) / 4;
+    hipLaunchKernelGGL(up::up_compact_init_kernel, dim3((unsigned)up::ceil_div(nwords, 256)),
+                       dim3(256), 0, stream, static_cast<uint32_t*>(ptr), nwords);
+    up_status st = up::check_launch("up_compact_init_kernel");
+    if (st != UP_OK) return st;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return UP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -921,6 +967,46 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
                positions, hidden_out,  positions_out,    cu_seqlens_out, out_capacity_rows,
                workspace, workspace_bytes, stream};
   return run_gather(c, T, false);
+}
+
+up_status up_compact_noalloc(int num_seqs, const int32_t* cu_seqlens_h,
+                             const int32_t* cu_seqlens_d, const int32_t* cu_blocks_d, int block,
+                             const uint8_t* block_mask, const void* hidden, int64_t row_bytes,
+                             int64_t row_stride_bytes, const int32_t* positions, void* hidden_out,
+                             int32_t* positions_out, int32_t* cu_seqlens_out,
+                             int64_t out_capacity_rows, int32_t* status, hipStream_t stream) {
+  up::clear_error();
+  int64_t T;
+  int max_len;
+  up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &max_len);
+  if (st != UP_OK) return st;
+  if (block < 1 || block > 4096) return up::set_error(UP_ERR_INVALID, "block not in [1, 4096]");
+  const CompactLayout lay = compact_layout(num_seqs, cu_seqlens_h, block);
+  if (lay.blocks > kScratchMaxBlocks || lay.bytes > kScratchBytes)
+    return up::set_error(UP_ERR_CAPACITY, "%lld blocks: up_compact_noalloc serves at most %lld",
+                         (long long)lay.blocks, (long long)kScratchMaxBlocks);
+  if (out_capacity_rows < T)
+    return up::set_error(UP_ERR_CAPACITY, "out_capacity_rows %lld < T %lld",
+                         (long long)out_capacity_rows, (long long)T);
+  if (!cu_seqlens_out || (T > 0 && (!hidden || !hidden_out)))
+    return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if ((positions == nullptr) != (positions_out == nullptr))
+    return up::set_error(UP_ERR_INVALID, "positions and positions_out must both be set or both NULL");
+  if (num_seqs == 0) return UP_OK;
+  st = up::check_device();
+  if (st != UP_OK) return st;
+  void* ws = nullptr;
+  st = scratch_for_current_device(stream, &ws);
+  if (st != UP_OK) return st;
+  GatherCall c{num_seqs,  cu_seqlens_h, cu_seqlens_d,     cu_blocks_d, block,
+               block_mask, hidden,      row_bytes,        row_stride_bytes,
+               positions, hidden_out,  positions_out,    cu_seqlens_out, out_capacity_rows,
+               ws,        kScratchBytes, stream};
+  st = run_gather(c, T, false);
+  if (st != UP_OK || status == nullptr) return st;
+  hipLaunchKernelGGL(up::up_compact_status_kernel, dim3(1), dim3(64), 0, stream,
+                     static_cast<uint32_t*>(ws), status, 1);
+  return up::check_launch("up_compact_status_kernel");
 }
 
 up_status up_revive(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
