@@ -12,8 +12,9 @@ G=64, p=0.99, 128 sink / 128 tail tokens, 5% planted blocks (seeded).
 Prints ONE JSON line (rank 0).  Besides the required fields it reports the
 roofline of the dominant kernel (HIP events on the stream the kernels run
 on), a per-call time breakdown, the scoring kernels' MFMA fraction, and the
-CPU oracle timed on the host on the same input bytes (with a full-size parity
-check of the GPU result against it).
+plain C++ CPU oracle timed on one pinned host core on a bounded sample of the
+same input bytes, and a full-size parity check of the GPU result against the
+numpy oracle.
 """
 from __future__ import annotations
 
@@ -47,7 +48,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (for profiler runs)")
     ap.add_argument("--cpu-threads", type=int, default=1,
-                    help="BLAS threads the oracle may use")
+                    help="BLAS threads of the numpy oracle in the full-size parity check")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference for counter scaling)")
     ap.add_argument("--stack", action="store_true",
@@ -584,55 +585,91 @@ def stack_bench(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8", errors="replace"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_leg(w, inp, ws, kept, threads, T):
-    """Time the CPU oracle on the same input bytes and check the GPU result."""
+    """The CPU baseline (the C++ oracle, one thread pinned to one core, on a
+    bounded sample of the bench batch) and a full-size parity check of the GPU
+    result against the numpy oracle (fp64, BLAS with `threads` threads, not
+    timed)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
 
     import oracle as O
+    import oracle.cxx as CX
 
     cu = inp["cu_seqlens"].numpy()
     lens = inp["lengths"]
-    q_bits = inp["q"].view(torch.int16)
+    q_bits = inp["q"].view(torch.int16).cpu().numpy()
+    k_bits = inp["k"].view(torch.int16).cpu().numpy()
+    hid = inp["hidden"].view(torch.int16).cpu().numpy()
+    pos = inp["positions"].cpu().numpy()
+
+    # --- CPU baseline: the plain single-threaded C++ oracle ---------------
+    # Sample: steps 1-2 for the query heads of KV head 0 (hq/hkv of the hq
+    # heads; scores are a sum over heads, so the full step costs hkv times
+    # as much and is scaled so), steps 3-5 on those scores over every token.
+    cx = CX.module()
+    group = w.hq // w.hkv
+    heads = list(range(group))
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[0]
+    os.sched_setaffinity(0, {core})      # this thread only (no re-exec)
+    try:
+        t0 = time.perf_counter()
+        c = cx.token_scores(q_bits, k_bits, cu, w.n_query, None, heads=heads)
+        bsc = cx.block_scores(c, cu, w.block)
+        t1 = time.perf_counter()
+        mask_s, _ = cx.select_topp(bsc, cu, w.block, w.top_p, w.sink, w.tail)
+        t2 = time.perf_counter()
+        _, _, cu_s = cx.compact(mask_s, hid, pos, cu, w.block)
+        t3 = time.perf_counter()
+        led = cx.history_new(len(lens))
+        cx.history_append(led, 0, cu_s)
+        t4 = time.perf_counter()
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    score_full = (t1 - t0) * w.hkv
+    total = score_full + (t4 - t1)
+    cpu = {"value": round(T / total, 1), "unit": "tokens/s", "cores": 1,
+           "kind": "oracle (plain C++17, fp64, single thread)",
+           "seconds": round(total, 2),
+           "seconds_per_step": {"score_s": round(score_full, 2),
+                                "score_sample_s": round(t1 - t0, 2),
+                                "select_s": round(t2 - t1, 3), "compact_s": round(t3 - t2, 3),
+                                "history_s": round(t4 - t3, 5)},
+           "sample": (f"the bench batch ({len(lens)} request(s), {T} tokens): steps 1-2 (scores, "
+                      f"block means) over the {group} query heads of KV head 0, timed and scaled by "
+                      f"hkv = {w.hkv} to all {w.hq} heads; steps 3-5 (Top-p, compaction of "
+                      f"{w.hidden_dim}-wide rows, ledger) on the whole batch; one thread pinned to "
+                      f"core {core} of {cpu_model()}; the process may use {len(allowed)} of the "
+                      f"host's {os.cpu_count()} logical CPUs")}
+
+    # --- full-size parity of this run: numpy oracle (fp64) vs the GPU -------
     q64 = np.zeros(tuple(inp["q"].shape), dtype=np.float64)   # untouched pages stay virtual
     for r, L in enumerate(lens):
         ne = min(w.n_query, L)
         s1 = int(cu[r + 1])
-        q64[s1 - ne:s1] = O.widen_bf16(q_bits[s1 - ne:s1].cpu().numpy())
-    k64 = O.widen_bf16(inp["k"].view(torch.int16).cpu().numpy())
-    hid = inp["hidden"].view(torch.int16).cpu().numpy()
-    pos = inp["positions"].cpu().numpy()
-    steps = {}
+        q64[s1 - ne:s1] = O.widen_bf16(q_bits[s1 - ne:s1])
+    k64 = O.widen_bf16(k_bits)
     with threadpool_limits(threads):
-        t0 = time.perf_counter()
         c = O.token_scores(q64, k64, cu, w.n_query, None)
         bsc = O.block_scores(c, cu, w.block)
-        t1 = time.perf_counter()
         mask, kept_ref = O.select_topp(bsc, cu, w.block, w.top_p, w.sink, w.tail)
-        t2 = time.perf_counter()
         h_out, p_out, cu_out = O.compact(mask, hid, pos, cu, w.block)
-        t3 = time.perf_counter()
-        led = O.history_new(len(lens))
-        O.history_append(led, 0, cu_out)
-        t4 = time.perf_counter()
-    dt = t4 - t0
-    steps = {"score_s": round(t1 - t0, 3), "select_s": round(t2 - t1, 3),
-             "compact_s": round(t3 - t2, 3), "history_s": round(t4 - t3, 4)}
+    del q64, k64
     out = {"token_scores": c, "block_scores": bsc, "mask": mask, "hidden_out": h_out,
            "positions_out": p_out, "cu_out": cu_out}
-    try:
-        import multiprocessing
-        host_cores = multiprocessing.cpu_count()
-    except Exception:
-        host_cores = None
-    cpu = {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-           "seconds": round(dt, 2), "seconds_per_step": steps,
-           "sample": f"the full bench batch ({len(lens)} request(s), {T} tokens): fp64 numpy oracle "
-                     f"score+select+compact+history, BLAS limited to {threads} thread(s); "
-                     f"host reports {host_cores} logical CPUs"}
-
-    # full-size parity of this run (oracle fp64 pipeline vs the GPU chain)
     gpu_ts = ws.token_scores[:T].double().cpu().numpy()
     ref = out["token_scores"]
     rel_err = np.abs(gpu_ts - ref) / np.abs(ref)

@@ -6,8 +6,9 @@ calls it, and it shares no code with the GPU library.
 
 Every function is a plain fp64 transcription of what the method computes, as
 described on the UniPrefill article page "中国科学院与腾讯微信合作解决AI排队等待问题"
-(sections 二 and 三 and its Q&A).  See uniprefill_oracle.py for per-function
-citations.
+(sections 二 and 三 and its Q&A).  Two implementations of steps 1-5:
+uniprefill_oracle.py (numpy) and uniprefill_oracle.cpp (plain single-threaded
+C++17, reached through cxx.py); see those files for per-function citations.
 """
 from .uniprefill_oracle import (  # noqa: F401
     widen_bf16,
