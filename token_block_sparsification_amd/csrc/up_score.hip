@@ -11,12 +11,12 @@
 //   pass A  up_rowstats_kernel   per (request, KV head, key chunk): bf16
 //           MFMA S tiles with keys on the MFMA M axis, so each lane owns one
 //           query row and reduces a running (max, sum) in registers.
-//   combine up_rowstats_combine_kernel  merges the chunk partials into one
-//           log2-domain bias per row: m * c + log2(l), c = scale * log2(e).
-//   pass B  up_colsum_kernel    same tiles with queries on the M axis, so each
-//           lane owns one key and sums exp2(s * c - bias) over its rows in
-//           registers; waves meet in LDS, one partial per (KV head, row group)
-//           is written per key.
+//   pass B  up_colsum_kernel    first merges the chunk partials of its rows
+//           into one log2-domain bias per row, m * c + log2(l) with
+//           c = scale * log2(e); then the same tiles with queries on the M
+//           axis, so each lane owns one key and sums exp2(s * c - bias) over
+//           its rows in registers; waves meet in LDS, one partial per (KV
+//           head, row group) is written per key.
 //   epilogue up_blockmean_kernel sums the partials over KV heads in a fixed
 //           order (token score) and averages each block (block score).
 // No floating-point atomics anywhere: results are bitwise reproducible.
@@ -55,11 +55,11 @@ struct ScoreArgs {
   int64_t q_tok, q_head, k_tok, k_head;
   int num_seqs, hq, hkv, rgqa, n_query, block;
   int ck, max_chunks, rg, rows_per_wg;
+  int ck_a;           // keys per row-statistics chunk (the partials' chunking)
   int64_t num_groups;  // real (request, KV head, key chunk) groups
   int reverse;         // walk the groups last to first
   float c;  // scale * log2(e)
-  float2* partial;  // [B][hq][n_query][max_chunks] (raw max, sum of exp2)
-  float* bias;      // [B][hkv][rgqa * n_query], row order of the KV group
+  float2* partial;  // [B][hq][max_chunks][n_query] (raw max, sum of exp2)
   float* colpart;   // [hkv * rg][T]
   int64_t T;
   float* token_scores;
@@ -600,47 +600,9 @@ up_rowstats_kernel(ScoreArgs a) {
     if (lane < 32 && rho < R) {
       const int hl = rho / n_eff, ti = rho - hl * n_eff;
       const int h = g * a.rgqa + hl;
-      a.partial[(((int64_t)req * a.hq + h) * a.n_query + ti) * a.max_chunks + chunk] =
+      a.partial[(((int64_t)req * a.hq + h) * a.max_chunks + chunk) * a.n_query + ti] =
           make_float2(M, l);
     }
-  }
-}
-
-// Combine the chunk partials of each row: bias = m * c + log2(l).  One wave
-// per row, lanes over chunks, fixed-order butterfly reductions.
-__global__ void __launch_bounds__(256) up_rowstats_combine_kernel(ScoreArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // The epilogue's per-request arrival counters start every call at zero.
-  if (blockIdx.x == 0)
-    for (int r = threadIdx.x; r < a.num_seqs; r += 256) {
-      a.arrive[r] = 0;
-      // a request without blocks never reaches the epilogue's selection
-      if (a.kept && a.cu_blocks[r + 1] == a.cu_blocks[r]) a.kept[r] = 0;
-    }
-  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t total = (int64_t)a.num_seqs * a.hq * a.n_query;
-  if (idx >= total) return;
-  const int ti = (int)(idx % a.n_query);
-  const int req = (int)(idx / ((int64_t)a.n_query * a.hq));
-  const int L = a.cu_seqlens[req + 1] - a.cu_seqlens[req];
-  const int n_eff = min(a.n_query, L);
-  if (ti >= n_eff) return;
-  const int nch = (L + a.ck - 1) / a.ck;
-  const float2* pp = a.partial + idx * a.max_chunks;
-  float M = kNegInf;
-  for (int c = lane; c < nch; c += 64) M = fmaxf(M, pp[c].x);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float mc = M * a.c;
-  float l = 0.f;
-  for (int c = lane; c < nch; c += 64) l += pp[c].y * fast_exp2(fmaf(pp[c].x, a.c, -mc));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-  // Stored in row order of the KV group: row rho = (h % rgqa) * n_eff + ti.
-  if (lane == 0) {
-    const int h = (int)(idx / a.n_query % a.hq);
-    const int g = h / a.rgqa, rho = (h - g * a.rgqa) * n_eff + ti;
-    a.bias[((int64_t)req * a.hkv + g) * a.rgqa * a.n_query + rho] = mc + log2f(l);
   }
 }
 
@@ -798,6 +760,17 @@ up_colsum_kernel(ScoreArgs a) {
   constexpr int KT = Tile::KT;
   __shared__ __attribute__((aligned(16))) uint16_t kl[RING][Tile::ELEMS];
   __shared__ float colbuf[2][W][64];
+  constexpr int ROWS = NT * 32 * W;
+  __shared__ float sbias[ROWS];
+
+  // The fused epilogue's per-request arrival counters start every call at
+  // zero (this kernel runs before that epilogue, after the previous call).
+  if (blockIdx.x == 0)
+    for (int r = threadIdx.x; r < a.num_seqs; r += 64 * W) {
+      a.arrive[r] = 0;
+      // a request without blocks never reaches the epilogue's selection
+      if (a.kept && a.cu_blocks[r + 1] == a.cu_blocks[r]) a.kept[r] = 0;
+    }
 
   const Work wk = decode_work(a);
   if (!wk.valid) return;
@@ -820,19 +793,53 @@ up_colsum_kernel(ScoreArgs a) {
   int ipos_unused[NT];
   load_q<D, NT>(a, s0, qpos0, n_eff, R, g, row0, lane, qf, ipos_unused);
 
+  // Softmax statistics of the workgroup's rows: one thread per row merges the
+  // row-statistics pass's chunk partials, in chunk order, into the
+  // log2-domain bias m * c + log2(l) (rows past R get +inf: probability 0).
+  // Every row's maximum is finite (chunk 0 holds key 0, which every tail row
+  // sees); chunks a row sees none of hold (-inf, 0) and add 0.
+  {
+    const int nch = (L + a.ck_a - 1) / a.ck_a;
+    for (int i = tid; i < ROWS; i += 64 * W) {
+      const int rho = wg_row0 + i;
+      float b = kPosInf;
+      if (rho < R) {
+        const int hl = rho / n_eff, ti = rho - hl * n_eff;
+        const float2* pp = a.partial + ((int64_t)req * a.hq + g * a.rgqa + hl) * a.max_chunks *
+                                           a.n_query + ti;
+        constexpr int CB = 8;  // partials loaded per batch (in flight together)
+        float M = kNegInf;
+        for (int c0 = 0; c0 < nch; c0 += CB) {
+          float x[CB];
+#pragma unroll
+          for (int u = 0; u < CB; ++u)
+            x[u] = c0 + u < nch ? pp[(int64_t)(c0 + u) * a.n_query].x : kNegInf;
+#pragma unroll
+          for (int u = 0; u < CB; ++u) M = fmaxf(M, x[u]);
+        }
+        const float mc = M * C;
+        float l = 0.f;
+        for (int c0 = 0; c0 < nch; c0 += CB) {
+          float2 v[CB];
+#pragma unroll
+          for (int u = 0; u < CB; ++u)
+            v[u] = c0 + u < nch ? pp[(int64_t)(c0 + u) * a.n_query] : make_float2(kNegInf, 0.f);
+#pragma unroll
+          for (int u = 0; u < CB; ++u) l += v[u].y * fast_exp2(fmaf(v[u].x, C, -mc));
+        }
+        b = mc + log2f(l);
+      }
+      sbias[i] = b;
+    }
+    __syncthreads();
+  }
   // Output element v of a 32x32 tile in lane l sits at row 8(v/4) + 4(l/32) + v%4.
-  // Row biases are stored in the KV group's row order; rows past R get +inf
-  // (probability 0).
-  const float* brow = a.bias + ((int64_t)req * a.hkv + g) * a.rgqa * a.n_query;
   float bv[NT][16];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rho = row0 + t * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const float b = brow[min(rho, R - 1)];
-      bv[t][v] = rho < R ? b : kPosInf;
-    }
+    for (int v = 0; v < 16; ++v)
+      bv[t][v] = sbias[row0 - wg_row0 + t * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)];
   }
 
   const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
@@ -1072,12 +1079,8 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, int ck_b, int64_t gro
                      dim3(64 * TA::W), 0, st, aa);
   up_status s = check_launch("up_rowstats_kernel");
   if (s != UP_OK) return s;
-  const int64_t rows = (int64_t)b_args.num_seqs * b_args.hq * b_args.n_query;
-  hipLaunchKernelGGL(up_rowstats_combine_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0,
-                     st, b_args);
-  s = check_launch("up_rowstats_combine_kernel");
-  if (s != UP_OK) return s;
   ScoreArgs bb = b_args;  // the column-sum pass chunks the keys its own way
+  bb.ck_a = b_args.ck;
   bb.ck = ck_b;
   bb.num_groups = groups_b;
   bb.reverse = UP_REVERSE_B;
@@ -1191,8 +1194,6 @@ up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int h
   size_t off = 0;
   g.off_partial = off;
   off = up::align_up(off + (size_t)num_seqs * hq * n_query * g.max_chunks * sizeof(float2), 256);
-  g.off_bias = off;
-  off = up::align_up(off + (size_t)num_seqs * hq * n_query * sizeof(float), 256);
   g.off_colpart = off;
   off = up::align_up(off + (size_t)hkv * g.rg * (size_t)T * sizeof(float), 256);
   g.off_arrive = off;
@@ -1306,7 +1307,6 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
   a.c = sc * 1.4426950408889634f;
   a.partial = reinterpret_cast<float2*>(ws + lay.g.off_partial);
-  a.bias = reinterpret_cast<float*>(ws + lay.g.off_bias);
   a.colpart = reinterpret_cast<float*>(ws + lay.g.off_colpart);
   a.T = T;
   a.token_scores = token_scores;
