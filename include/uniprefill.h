@@ -73,7 +73,9 @@ typedef enum up_status {
 } up_status;
 
 /* Element type of the entry points that compute on row elements (the
- * compaction and revival copies move bytes and take no element type). */
+ * compaction and revival copies move bytes and take no element type).  They
+ * take it as an int holding one of these values, so an out-of-range value is
+ * rejected (UP_ERR_INVALID) rather than read as an enum. */
 typedef enum up_dtype {
   UP_DTYPE_BF16 = 0,
   UP_DTYPE_F16 = 1,
@@ -409,7 +411,7 @@ up_status up_score_select(int num_seqs, const int32_t* cu_seqlens_h, const int32
  */
 up_status up_compact_rmsnorm(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                              const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
-                             up_dtype dtype, const void* hidden, int64_t hidden_dim,
+                             int dtype, const void* hidden, int64_t hidden_dim,
                              int64_t row_stride, const void* gamma, float eps,
                              const int32_t* positions, void* normed_out, void* residual_out,
                              int32_t* positions_out, int32_t* cu_seqlens_out,
@@ -431,7 +433,7 @@ up_status up_compact_rmsnorm(int num_seqs, const int32_t* cu_seqlens_h, const in
  */
 up_status up_gather_add(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                         const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
-                        up_dtype dtype, const void* frozen, int64_t hidden_dim, int64_t row_stride,
+                        int dtype, const void* frozen, int64_t hidden_dim, int64_t row_stride,
                         const void* delta, void* out, int64_t out_rows, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 

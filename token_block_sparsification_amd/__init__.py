@@ -29,7 +29,10 @@ __all__ = [
     "Batch", "Workspace", "run_chain",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuniprefill.so")
+# The in-tree library; UNIPREFILL_LIBRARY names another build of it (for
+# example one with host-side sanitizers).
+LIB_PATH = os.environ.get("UNIPREFILL_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libuniprefill.so")
 
 UP_OK = 0
 _STATUS = {0: "UP_OK", 1: "UP_ERR_INVALID", 2: "UP_ERR_UNSUPPORTED", 3: "UP_ERR_WORKSPACE",

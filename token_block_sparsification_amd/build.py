@@ -39,22 +39,46 @@ def _run(cmd, verbose):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every csrc/*.hip and link libuniprefill.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer: every -fsanitize is
+# preceded by -Xarch_host, so only the host code (argument checks, workspace
+# layouts, chunk rules, launch set-up) is instrumented; device code is built
+# as usual.  The library then needs the clang ASan runtime (which also holds
+# the UBSan handlers) loaded first, e.g. LD_PRELOAD.
+HOST_SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime matching hipcc's clang."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    return subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                          stdout=subprocess.PIPE, text=True, check=True).stdout.strip()
+
+
+def build(verbose: bool = False, jobs: int = 4, out: str = LIB, objdir: str = OBJDIR,
+          host_sanitize: bool = False) -> str:
+    """Compile every csrc/*.hip and link the library `out`; returns its path.
+    host_sanitize: instrument the host code with ASan + UBSan (see above)."""
+    os.makedirs(objdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
-    objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    flags = HIP_FLAGS + (HOST_SANITIZE_FLAGS if host_sanitize else [])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [HIPCC, *HIP_FLAGS, "-c", s, "-o", o], verbose)
+        futs = [ex.submit(_run, [HIPCC, *flags, "-c", s, "-o", o], verbose)
                 for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -836,10 +836,13 @@ void launch_rowop(up_dtype dt, const up::RowOpArgs& a, int64_t num_blocks, int b
 
 // Checks shared by the fused row operations: element type, row geometry in
 // 16-byte vectors (at most 16 KiB per row), 16-byte alignment of every row.
-up_status check_rows(up_dtype dt, int64_t hidden_dim, std::initializer_list<int64_t> strides,
+// dtype arrives as a plain int from the C ABI and is checked before it is
+// converted to up_dtype.
+up_status check_rows(int dtype, int64_t hidden_dim, std::initializer_list<int64_t> strides,
                      std::initializer_list<const void*> ptrs) {
-  if (dt != UP_DTYPE_BF16 && dt != UP_DTYPE_F16 && dt != UP_DTYPE_F32)
-    return up::set_error(UP_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (dtype != UP_DTYPE_BF16 && dtype != UP_DTYPE_F16 && dtype != UP_DTYPE_F32)
+    return up::set_error(UP_ERR_INVALID, "unknown dtype %d", dtype);
+  const up_dtype dt = static_cast<up_dtype>(dtype);
   if (hidden_dim < 1) return up::set_error(UP_ERR_INVALID, "hidden_dim < 1");
   const int64_t rb = hidden_dim * elem_bytes(dt);
   if (rb % 16 != 0 || rb > 16384)
@@ -1029,7 +1032,7 @@ up_status up_revive(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu
 
 up_status up_compact_rmsnorm(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                              const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
-                             up_dtype dtype, const void* hidden, int64_t hidden_dim,
+                             int dtype_value, const void* hidden, int64_t hidden_dim,
                              int64_t row_stride, const void* gamma, float eps,
                              const int32_t* positions, void* normed_out, void* residual_out,
                              int32_t* positions_out, int32_t* cu_seqlens_out,
@@ -1048,9 +1051,10 @@ up_status up_compact_rmsnorm(int num_seqs, const int32_t* cu_seqlens_h, const in
   if ((positions == nullptr) != (positions_out == nullptr))
     return up::set_error(UP_ERR_INVALID, "positions and positions_out must both be set or both NULL");
   if (!(eps >= 0.f) || !isfinite(eps)) return up::set_error(UP_ERR_INVALID, "eps must be finite and >= 0");
-  st = check_rows(dtype, hidden_dim, {row_stride, hidden_dim},
+  st = check_rows(dtype_value, hidden_dim, {row_stride, hidden_dim},
                   {hidden, normed_out, residual_out, gamma});
   if (st != UP_OK) return st;
+  const up_dtype dtype = static_cast<up_dtype>(dtype_value);
   const int64_t eb = elem_bytes(dtype);
   GatherCall c{num_seqs,  cu_seqlens_h, cu_seqlens_d,  cu_blocks_d,    block,
                block_mask, hidden,      hidden_dim * eb, row_stride * eb, positions,
@@ -1081,7 +1085,7 @@ up_status up_compact_rmsnorm(int num_seqs, const int32_t* cu_seqlens_h, const in
 
 up_status up_gather_add(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                         const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
-                        up_dtype dtype, const void* frozen, int64_t hidden_dim, int64_t row_stride,
+                        int dtype_value, const void* frozen, int64_t hidden_dim, int64_t row_stride,
                         const void* delta, void* out, int64_t out_rows, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
   up::clear_error();
@@ -1092,8 +1096,9 @@ up_status up_gather_add(int num_seqs, const int32_t* cu_seqlens_h, const int32_t
   if (out_rows < 0) return up::set_error(UP_ERR_INVALID, "out_rows < 0");
   if (T > 0 && out_rows > 0 && (!frozen || !delta || !out))
     return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
-  st = check_rows(dtype, hidden_dim, {row_stride, hidden_dim}, {frozen, delta, out});
+  st = check_rows(dtype_value, hidden_dim, {row_stride, hidden_dim}, {frozen, delta, out});
   if (st != UP_OK) return st;
+  const up_dtype dtype = static_cast<up_dtype>(dtype_value);
   const int64_t eb = elem_bytes(dtype);
   GatherCall c{num_seqs, cu_seqlens_h, cu_seqlens_d,    cu_blocks_d,     block,
                block_mask, frozen,     hidden_dim * eb, row_stride * eb, nullptr,
