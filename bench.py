@@ -72,15 +72,16 @@ def source_sha(names) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, src: str, launches_per_call: int = 1):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
-    the kernel's source changed since they were taken."""
+def load_traffic(kernel: str, src: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs of this
+    workload, or None when they were taken on another workload or the
+    kernel's source changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != source_sha(src):
+    if not rec or rec.get("source_sha") != source_sha(src) or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -100,7 +101,7 @@ TRAFFIC_KERNELS = {
 }
 
 
-def write_traffic(fetch_csv: str, write_csv: str) -> None:
+def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> None:
     """HBM bytes per dispatch of the path's kernels from FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch), each scaled by the factor that makes the plain copy of
     COPY_BYTES read and write exactly COPY_BYTES."""
@@ -131,7 +132,7 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
             vals = [x for n, v in per.items() if re.search(pat, n) for x in v]
             if not vals:
                 continue
-            rec = out.setdefault(short, {"source_sha": source_sha(src),
+            rec = out.setdefault(short, {"source_sha": source_sha(src), "workload": workload,
                                          "source": src if isinstance(src, str) else "+".join(src)})
             rec[key + "_bytes_per_launch"] = sum(vals) / len(vals) * scale
             rec[key + "_scale"] = scale
@@ -146,7 +147,7 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
 def main():
     args = parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(*args.write_traffic, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py: the path runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -393,8 +394,8 @@ def main():
         # The copy kernel moves every byte; the events bracket the whole
         # up_compact call (its small scan launch included), so `achieved`
         # slightly understates the copy kernel's own rate.
-        tc = load_traffic("up_compact_copy_kernel", "up_compact.hip")
-        ts = load_traffic("up_compact_scan_kernel", "up_compact.hip")
+        tc = load_traffic("up_compact_copy_kernel", "up_compact.hip", w.name)
+        ts = load_traffic("up_compact_scan_kernel", "up_compact.hip", w.name)
         traffic = tc + ts if tc is not None and ts is not None else None
         roofline = {"kernel": "up_compact_copy_kernel", "bound": "hbm", "achieved": round(compact_gbs, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
@@ -403,7 +404,7 @@ def main():
                     "duration": ("HIP events around up_compact (scan + copy launches) on every "
                                  f"{EVENT_EVERY}th step of the timed region ({len(dom_all)} launches)")}
     else:
-        roofline = {"kernel": "up_score (rowstats+combine+colsum+blockmean)", "bound": "mfma",
+        roofline = {"kernel": "up_score (rowstats+colsum+blockmean)", "bound": "mfma",
                     "achieved": round(score_tflops_exec, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(score_tflops_exec / PEAK_BF16_TFLOPS, 4),
                     "traffic": None, "algorithmic_flops_per_launch": flops_exec}
@@ -425,8 +426,8 @@ def main():
         "up_compact_rmsnorm_frac_of_hbm_peak": round(gbs(norm_bytes, fz_us["up_compact_rmsnorm"]) / PEAK_HBM_GBS, 4),
         "up_compact_rmsnorm_algorithmic_bytes": int(norm_bytes),
         "up_compact_rmsnorm_traffic": (lambda a, b: a + b if a is not None and b is not None else None)(
-            load_traffic("up_rowop_kernel_norm", "up_compact.hip"),
-            load_traffic("up_compact_scan_kernel", "up_compact.hip")),
+            load_traffic("up_rowop_kernel_norm", "up_compact.hip", w.name),
+            load_traffic("up_compact_scan_kernel", "up_compact.hip", w.name)),
         "up_gather_add_us": round(fz_us["up_gather_add"], 2),
         "up_gather_add_gbs": gbs(add_bytes, fz_us["up_gather_add"]),
         "up_gather_add_frac_of_hbm_peak": round(gbs(add_bytes, fz_us["up_gather_add"]) / PEAK_HBM_GBS, 4),
@@ -476,8 +477,8 @@ def main():
                                              / 1e9 / PEAK_HBM_GBS, 4),
                    "algorithmic_bytes": int(compact_bytes_rv),
                    "traffic": (lambda a, b: a + b if a is not None and b is not None else None)(
-                       load_traffic("up_revive_copy_kernel", "up_compact.hip"),
-                       load_traffic("up_compact_scan_kernel", "up_compact.hip"))},
+                       load_traffic("up_revive_copy_kernel", "up_compact.hip", w.name),
+                       load_traffic("up_compact_scan_kernel", "up_compact.hip", w.name))},
         "kv_len_us": round(med_us(rv_marks, "up_kv_len"), 2),
         "graph_step_us": round(graph_step_us, 2),
         "fused_pipeline": fused_rec,
@@ -616,18 +617,24 @@ def cpu_leg(w, inp, ws, kept, threads, T):
     pos = inp["positions"].cpu().numpy()
 
     # --- CPU baseline: the plain single-threaded C++ oracle ---------------
-    # Sample: steps 1-2 for the query heads of KV head 0 (hq/hkv of the hq
-    # heads; scores are a sum over heads, so the full step costs hkv times
-    # as much and is scaled so), steps 3-5 on those scores over every token.
+    # Sample: steps 1-2 for the query heads of KV heads 0, 1, ... (hq/hkv
+    # query heads each), one KV group at a time until at least ten seconds of
+    # CPU work are timed; scores are a sum over heads, so the full step costs
+    # hkv / (groups timed) times as much and is scaled so.  Steps 3-5 then run
+    # on those partial scores over every token.
     cx = CX.module()
     group = w.hq // w.hkv
-    heads = list(range(group))
     allowed = sorted(os.sched_getaffinity(0))
     core = allowed[0]
     os.sched_setaffinity(0, {core})      # this thread only (no re-exec)
     try:
         t0 = time.perf_counter()
-        c = cx.token_scores(q_bits, k_bits, cu, w.n_query, None, heads=heads)
+        c = np.zeros(T, dtype=np.float64)
+        groups = 0
+        while groups < w.hkv and (groups == 0 or time.perf_counter() - t0 < 10.0):
+            heads = list(range(groups * group, (groups + 1) * group))
+            c += cx.token_scores(q_bits, k_bits, cu, w.n_query, None, heads=heads)
+            groups += 1
         bsc = cx.block_scores(c, cu, w.block)
         t1 = time.perf_counter()
         mask_s, _ = cx.select_topp(bsc, cu, w.block, w.top_p, w.sink, w.tail)
@@ -639,21 +646,23 @@ def cpu_leg(w, inp, ws, kept, threads, T):
         t4 = time.perf_counter()
     finally:
         os.sched_setaffinity(0, set(allowed))
-    score_full = (t1 - t0) * w.hkv
+    score_full = (t1 - t0) * w.hkv / groups
     total = score_full + (t4 - t1)
     cpu = {"value": round(T / total, 1), "unit": "tokens/s", "cores": 1,
            "kind": "oracle (plain C++17, fp64, single thread)",
            "seconds": round(total, 2),
+           "seconds_timed": round(t4 - t0, 2),
            "seconds_per_step": {"score_s": round(score_full, 2),
                                 "score_sample_s": round(t1 - t0, 2),
                                 "select_s": round(t2 - t1, 3), "compact_s": round(t3 - t2, 3),
                                 "history_s": round(t4 - t3, 5)},
            "sample": (f"the bench batch ({len(lens)} request(s), {T} tokens): steps 1-2 (scores, "
-                      f"block means) over the {group} query heads of KV head 0, timed and scaled by "
-                      f"hkv = {w.hkv} to all {w.hq} heads; steps 3-5 (Top-p, compaction of "
-                      f"{w.hidden_dim}-wide rows, ledger) on the whole batch; one thread pinned to "
-                      f"core {core} of {cpu_model()}; the process may use {len(allowed)} of the "
-                      f"host's {os.cpu_count()} logical CPUs")}
+                      f"block means) over the {groups * group} query heads of KV heads "
+                      f"0..{groups - 1}, timed and scaled by hkv/{groups} = {w.hkv / groups:g} to "
+                      f"all {w.hq} heads; steps 3-5 (Top-p, compaction of {w.hidden_dim}-wide "
+                      f"rows, ledger) on the whole batch; one thread pinned to core {core} of "
+                      f"{cpu_model()}; the process may use {len(allowed)} of the host's "
+                      f"{os.cpu_count()} logical CPUs")}
 
     # --- full-size parity of this run: numpy oracle (fp64) vs the GPU -------
     q64 = np.zeros(tuple(inp["q"].shape), dtype=np.float64)   # untouched pages stay virtual

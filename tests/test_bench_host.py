@@ -48,7 +48,7 @@ def test_write_traffic_scales_by_the_copy_probe(tmp_path, monkeypatch):
                                        (scan, 8.0)])
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
-    bench.write_traffic(str(fetch), str(write))
+    bench.write_traffic(str(fetch), str(write), "llama8b_L131072")
     rec = json.loads(out.read_text())
     c = rec["up_compact_copy_kernel"]
     assert c["fetch_scale"] == pytest.approx(2.0)
@@ -61,9 +61,12 @@ def test_write_traffic_scales_by_the_copy_probe(tmp_path, monkeypatch):
     assert s["bytes_per_launch"] == pytest.approx((4.0 * 2.0 + 8.0) * 1024)
     assert "up_revive_copy_kernel" not in rec  # no dispatch of it in the CSVs
     # the stored figure is used only while the kernel's source is unchanged
-    assert bench.load_traffic("up_compact_copy_kernel", "up_compact.hip") == c["bytes_per_launch"]
+    assert bench.load_traffic("up_compact_copy_kernel", "up_compact.hip", "llama8b_L131072") \
+        == c["bytes_per_launch"]
+    # ... and on the workload the counters were taken on
+    assert bench.load_traffic("up_compact_copy_kernel", "up_compact.hip", "llama8b_L32768") is None
     rec["up_compact_copy_kernel"]["source_sha"] = "0" * 16
     out.write_text(json.dumps(rec))
-    assert bench.load_traffic("up_compact_copy_kernel", "up_compact.hip") is None
-    assert bench.load_traffic("no_such_kernel", "up_compact.hip") is None
+    assert bench.load_traffic("up_compact_copy_kernel", "up_compact.hip", "llama8b_L131072") is None
+    assert bench.load_traffic("no_such_kernel", "up_compact.hip", "llama8b_L131072") is None
 
