@@ -103,6 +103,36 @@ def test_long_chunk_boundaries():
     _end_to_end(W.make_inputs(w), 128, 64, name=w.name)
 
 
+def _column_sum_chunk(lengths, hkv, rg):
+    """The column-sum pass's key chunk before it is rounded to whole blocks
+    (the host rule: whole rounds of 512 workgroups, chunks of 256 + 64 i keys
+    minimising rounds x (chunk + 256), longer on ties), given the row-statistics
+    chunk 256 that these test batches get."""
+    per_round = max(1, 512 // (hkv * rg))
+    best, best_ck = None, 256
+    for ck in range(256, 4097, 64):
+        nch = sum(-(-L // ck) for L in lengths)
+        cost = -(-nch // per_round) * (ck + 256)
+        if best is None or cost <= best:
+            best, best_ck = cost, ck
+    return best_ck
+
+
+@pytest.mark.parametrize("G", [128, 256])
+def test_chunks_rounded_to_whole_blocks(G):
+    """The column-sum chunk that the rounds rule picks (320 keys here) holds no
+    whole number of 128- or 256-token blocks; the pass rounds it up so that
+    every chunk's last workgroup can average whole blocks.  Ragged requests,
+    a 3000-token one with a short last block."""
+    lengths = (9000, 7000, 5000, 12000, 3000)
+    ck = _column_sum_chunk(lengths, hkv=2, rg=2)
+    assert ck == 320 and ck % G != 0
+    w = W.Workload(name=f"rounded_chunks_G{G}", lengths=lengths, hq=8, hkv=2, head_dim=128,
+                   hidden_dim=64, hidden_dtype="bf16", seed=6150 + G, plant_frac=0.05,
+                   num_seqs=len(lengths))
+    _end_to_end(W.make_inputs(w), 128, G, name=w.name)
+
+
 def test_tail_equals_n_and_small_p():
     w = W.Workload(name="p_sweep", lengths=(4096, 2000), hq=8, hkv=2, head_dim=128, hidden_dim=32,
                    hidden_dtype="bf16", seed=6001, plant_frac=0.1, num_seqs=2)

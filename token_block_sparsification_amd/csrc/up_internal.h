@@ -35,7 +35,8 @@ struct ScoreGeometry {
   int ck;            // keys per row-statistics workgroup chunk (sets the partials layout)
   int ck_b;          // keys per column-sum workgroup chunk
   int max_chunks;    // chunks of the longest request
-  size_t off_partial, off_colpart, off_arrive, bytes;
+  int chunks_b;      // column-sum chunk counters per request (chunks of >= 256 keys)
+  size_t off_partial, off_colpart, off_arrive, off_chunk_arrive, bytes;
 };
 
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv,

@@ -1,13 +1,14 @@
 // Step 4 of the pruning path: Top-p block selection with forced blocks, one
 // workgroup per request (the rule and the algorithm are described in
-// up_select_impl.h, which the scoring epilogue shares).
+// up_select_impl.h, which the column-sum kernel of the fused entry point
+// shares).
 #include "up_select_impl.h"
 
 namespace up {
 namespace {
 
 __global__ void __launch_bounds__(kSelectThreads) up_select_kernel(SelectArgs a) {
-  __shared__ SelectShared sh;
+  __shared__ SelectShared<kSelectThreads, kStageMax> sh;
   select_request(a, blockIdx.x, sh);
 }
 

@@ -29,9 +29,11 @@
 //   4. Blocks with score v* are tied; the lowest-index ones are kept until the
 //      mass reaches R: each thread takes a contiguous run of blocks, and one
 //      block-wide exclusive scan of the runs' tie counts ranks every tie.
-// A request with at most kStageMax blocks has its keys and fixed-point masses
+// A request with at most STAGE blocks has its keys and fixed-point masses
 // computed once into LDS (every later pass reads them there); longer requests
-// recompute them from the scores in memory on every pass.
+// recompute them from the scores in memory on every pass.  The workgroup
+// size NTH and STAGE are template arguments, so the column-sum kernel can run
+// the selection with its own workgroup, its state in the K ring's LDS.
 // Fixed point differs from exact fp64 sums by < N * 2^-S of the top score, so
 // a decision can differ from an fp64 evaluation only when the cumulative
 // mass is within that distance of p * total.
@@ -48,9 +50,8 @@ namespace {
 #define UP_SEL_THREADS 512
 #endif
 constexpr int kSelectThreads = UP_SEL_THREADS;
-constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int64_t kMaxBlocksPerRequest = 1 << 24;
-constexpr int kStageMax = 4096;         // blocks staged in LDS
+constexpr int kStageMax = 4096;         // blocks staged in LDS by the stand-alone kernel
 #ifndef UP_SEL_DIGIT_BITS
 #define UP_SEL_DIGIT_BITS 8
 #endif
@@ -89,15 +90,18 @@ __device__ __forceinline__ uint64_t mass_of(float s, double scale) {
   return m > 0.0 ? (uint64_t)m : 0ull;
 }
 
+template <int NTH, int STAGE>
 struct SelectShared {
-  uint32_t skey[kStageMax];   // staged: order-preserving key (0 for forced blocks)
-  uint64_t smass[kStageMax];  // staged: fixed-point mass
+  static constexpr int kWaves = NTH / 64;
+  static constexpr int kStage = STAGE;
+  uint32_t skey[STAGE];   // staged: order-preserving key (0 for forced blocks)
+  uint64_t smass[STAGE];  // staged: fixed-point mass
   uint32_t cnt[2][kBucketSlots];
   uint64_t mass[2][kBucketSlots];
-  uint64_t red64[2][kSelectWaves];
-  float redf[kSelectWaves];
-  uint32_t redu[2][kSelectWaves];
-  int redi[kSelectWaves];
+  uint64_t red64[2][kWaves];
+  float redf[kWaves];
+  uint32_t redu[2][kWaves];
+  int redi[kWaves];
   // decision state (written by wave 0, read by all after a barrier)
   uint32_t prefix;       // known high bits of the cutoff key
   uint64_t above;        // optional mass with key above the current bucket range
@@ -117,7 +121,8 @@ __device__ __forceinline__ T wave_sum(T v) {
 // bucket where above + (mass of this and higher buckets) >= need; refine the
 // state.  Bucket d of this pass holds keys whose bits [shift, shift + width)
 // equal d (higher bits equal the known prefix).
-__device__ void pick_bucket(SelectShared& sh, int buf, int shift, int width, uint64_t need) {
+template <typename Shared>
+__device__ void pick_bucket(Shared& sh, int buf, int shift, int width, uint64_t need) {
   const int lane = threadIdx.x & 63;
   const int nbk = 1 << width;
   // lane l owns buckets top-kBucketsPerLane*l ... (highest first)
@@ -162,11 +167,23 @@ __device__ void pick_bucket(SelectShared& sh, int buf, int shift, int width, uin
   }
 }
 
-// Selection of one request by the whole (kSelectThreads-thread) workgroup.
-// STAGED: the request has at most kStageMax blocks; their keys and masses
-// are computed once into LDS and every later pass reads them from there.
-template <bool STAGED>
-__device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared& sh) {
+// Block score i of a request: COHERENT reads it with a relaxed device-scope
+// atomic load, for scores written earlier in the same kernel by workgroups
+// on other XCDs (the column-sum kernel of the fused entry point).
+template <bool COHERENT>
+__device__ __forceinline__ float score_at(const float* sc, int i) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(sc + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return sc[i];
+}
+
+// Selection of one request by the whole (NTH-thread) workgroup.
+// STAGED: the request has at most STAGE blocks; their keys and masses are
+// computed once into LDS and every later pass reads them from there.
+template <bool STAGED, int NTH, int STAGE, bool COHERENT>
+__device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared<NTH, STAGE>& sh) {
+  constexpr int kSelectThreads = NTH;
+  constexpr int kSelectWaves = NTH / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s0 = a.cu_seqlens[req];
   const int L = a.cu_seqlens[req + 1] - s0;
@@ -178,7 +195,7 @@ __device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared& 
   float mx = 0.f;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int i = tid; i < nb; i += kSelectThreads) {
-    const float s = sc[i];
+    const float s = score_at<COHERENT>(sc, i);
     if (STAGED) sh.skey[i] = __float_as_uint(s);
     mx = fmaxf(mx, s);
     if (!is_forced(i, L, G, a.sink, a.tail)) {
@@ -221,7 +238,7 @@ __device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared& 
       return true;
     }
     if (is_forced(i, L, G, a.sink, a.tail)) return false;
-    const float s = sc[i];
+    const float s = score_at<COHERENT>(sc, i);
     key = orderable(s);
     m = mass_of(s, scale);
     return true;
@@ -231,7 +248,7 @@ __device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared& 
   //    masses into LDS (each thread rewrites the entries it staged)
   uint64_t tot = 0, forced = 0;
   for (int i = tid; i < nb; i += kSelectThreads) {
-    const float s = STAGED ? __uint_as_float(sh.skey[i]) : sc[i];
+    const float s = STAGED ? __uint_as_float(sh.skey[i]) : score_at<COHERENT>(sc, i);
     const uint64_t m = mass_of(s, scale);
     const bool f = is_forced(i, L, G, a.sink, a.tail);
     tot += m;
@@ -355,17 +372,18 @@ __device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared& 
   }
 }
 
-// Selection of one request by the whole (kSelectThreads-thread) workgroup.
+// Selection of one request by the whole (NTH-thread) workgroup.
 // Uniform over the workgroup; every thread must call it.
-__device__ void select_request(const SelectArgs& a, int req, SelectShared& sh) {
+template <int NTH, int STAGE, bool COHERENT = false>
+__device__ void select_request(const SelectArgs& a, int req, SelectShared<NTH, STAGE>& sh) {
   const int nb = a.cu_blocks[req + 1] - a.cu_blocks[req];
   if (nb <= 0) {
     if (threadIdx.x == 0) a.kept[req] = 0;
     return;
   }
   __syncthreads();  // the shared state may still be read by a previous call
-  if (nb <= kStageMax) select_impl<true>(a, req, nb, sh);
-  else select_impl<false>(a, req, nb, sh);
+  if (nb <= STAGE) select_impl<true, NTH, STAGE, COHERENT>(a, req, nb, sh);
+  else select_impl<false, NTH, STAGE, COHERENT>(a, req, nb, sh);
 }
 
 }  // namespace
