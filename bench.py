@@ -302,8 +302,8 @@ def main():
             rv_marks.append(m)
     torch.cuda.synchronize()
 
-    # Fused pipeline, outside the timed region: selection in the scoring
-    # epilogue, and the next layer's normalised operand / residual sum read
+    # Fused pipeline, outside the timed region: selection in the column-sum
+    # kernel, and the next layer's normalised operand / residual sum read
     # straight from the frozen rows, against the unfused calls (compaction,
     # then torch's RMSNorm of the compacted rows).
     D = hidden.shape[1]

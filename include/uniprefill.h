@@ -17,7 +17,7 @@
  *   up_kv_len       per-layer KV length read back from the ledger
  *   up_revive       scatter of packed kept rows back into the full buffer
  * and, fused:
- *   up_score_select     up_score + up_select_topp, selection in the epilogue
+ *   up_score_select     up_score + up_select_topp, selecting in the column-sum kernel
  * and, fused into the next layer's first reads (no compacted copy),
  *   up_compact_rmsnorm  normalised input operand of the kept rows
  *   up_gather_add       residual sum with the residual read from frozen rows
@@ -349,20 +349,22 @@ up_status up_revive(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
-/* Fused pipeline: selection inside the scoring epilogue (§三)               */
+/* Fused pipeline: selection inside the column-sum kernel (§三)              */
 /* ------------------------------------------------------------------------ */
 
 /*
- * up_score_select — up_score followed by up_select_topp in one call, with
- * the selection run by the scoring epilogue itself: the workgroup that
- * finishes the last block score of a request selects that request's blocks
- * (§三: scores, block aggregation and the binary mask without a round trip).
+ * up_score_select — up_score followed by up_select_topp in one call of two
+ * launches (§三: scores, block aggregation and the binary mask without a
+ * round trip).  The last of a key chunk's column-sum workgroups to finish
+ * computes the chunk's token and block scores, and the workgroup that
+ * finishes a request's last chunk selects that request's blocks.
  * Outputs are bit-identical to up_score then up_select_topp with the same
- * arguments (the same device code selects on the same block scores).
- * Arguments: those of up_score, then those of up_select_topp.  The
- * workspace is up_score's (it holds one arrival counter per request, reset
- * by every call; calls sharing a workspace run one at a time).  Requests
- * with no tokens get kept_tokens 0.
+ * arguments (same sums in the same order; the same selection code on the
+ * same block scores).  Arguments: those of up_score, then those of
+ * up_select_topp.  The workspace is up_score's (it holds the arrival
+ * counters, reset by every call; calls sharing a workspace run one at a
+ * time).  Requests with no tokens get kept_tokens 0.  At most 2^24 blocks
+ * per request, as for up_select_topp.
  */
 up_status up_score_select(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
                           const int32_t* cu_blocks_d, const void* q, int64_t q_tok_stride,
