@@ -277,10 +277,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Ring start: fetch tiles 0..2 (as many as exist), wait for tiles 0 and 1.
-template <typename Stream>
-__device__ __forceinline__ void ring_prologue(const Stream& ks, int ntiles,
-                                              uint16_t (*kl)[Stream::Tile::ELEMS]);
 // Wait until at most N of this wave's vector-memory loads (the K tile
 // fetches) are in flight.  Written as an asm statement so the compiler's own
 // wait-count pass keeps it exactly as placed.
@@ -297,14 +293,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the next iteration needs.  Loads return in issue order, so waiting until at
 // most (RING-3) tiles' worth of loads are outstanding is enough (stores the
 // pass issues in between only make that wait longer, never shorter).
+//
+// Ring start, in two parts so that a kernel's other prologue loads (query
+// rows, softmax statistics) travel together with the first tiles:
+// ring_issue fetches tiles 0 .. RING-2 (as many as exist); ring_ready then
+// waits until tiles 0 and 1 have landed.  Loads issued between the two only
+// make ring_ready's wait stronger (they complete after the tiles), never
+// weaker.
 template <int RING, typename Stream>
-__device__ __forceinline__ void ring_prologue(const Stream& ks, int ntiles,
-                                              uint16_t (*kl)[Stream::Tile::ELEMS]) {
+__device__ __forceinline__ void ring_issue(const Stream& ks, int ntiles,
+                                           uint16_t (*kl)[Stream::Tile::ELEMS]) {
   static_assert(RING >= 4 && RING % 2 == 0, "ring of an even number of slots, at least 4");
 #pragma unroll
   for (int t = 0; t < RING - 1; ++t)
     if (t < ntiles) ks.fetch(t, kl[t]);
-  if (ntiles >= RING - 1) wait_vmcnt<(RING - 3) * Stream::Tile::INSTS>();
+}
+template <int RING, typename Tile>
+__device__ __forceinline__ void ring_ready(int ntiles) {
+  if (ntiles >= RING - 1) wait_vmcnt<(RING - 3) * Tile::INSTS>();
   else wait_vmcnt<0>();
   lds_barrier();
 }
@@ -572,6 +578,13 @@ up_rowstats_kernel(ScoreArgs a) {
   const int qpos0 = L - n_eff;
   const float C = a.c;
 
+  // the first K tiles travel together with the query rows
+  const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
+  const int ntiles = (key1 - key0 + KT - 1) / KT;
+  KStream<D, W> ks;
+  ks.init(kbase, a.k_tok, key0, key1, wave, lane);
+  ring_issue<RING>(ks, ntiles, kl);
+
   bf16x8_t qf[NT][D / 16];
   int ipos[NT];
   load_q<D, NT>(a, s0, qpos0, n_eff, R, g, row0, lane, qf, ipos);
@@ -583,16 +596,12 @@ up_rowstats_kernel(ScoreArgs a) {
     l_run[t] = 0.f;
   }
 
-  const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
-  const int ntiles = (key1 - key0 + KT - 1) / KT;
   // leading tiles that need no mask: every key < key1 and <= every tail row
   const int lim = min(key1, qpos0 + 1);
   const int nfast = lim > key0 ? (lim - key0) / KT : 0;
   bf16x8_t af[D / 16];
   int it = 0;
-  KStream<D, W> ks;
-  ks.init(kbase, a.k_tok, key0, key1, wave, lane);
-  ring_prologue<RING>(ks, ntiles, kl);
+  ring_ready<RING, Tile>(ntiles);
 
   // Mask-free tiles first (software-pipelined when PIPE), then the tiles
   // that meet the causal diagonal or the chunk's end, in straight order.
@@ -661,21 +670,33 @@ up_rowstats_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 template <int NT>
 __device__ __forceinline__ float colsum_update(f32x16_t acc, int t, bool masked, int key, int key1,
-                                               int lane, int row0, int R, int n_eff, int qpos0,
-                                               float C, const float (&bv)[NT][16]) {
+                                               int lane, int row0, int n_eff, int qpos0, float C,
+                                               const float (&bv)[NT][16]) {
   float e[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], C, -bv[t][v]));
   if (masked) {
     // Rebuilt on every masked tile from an opaque base, so the compiler does
-    // not keep 16*NT row positions alive across the whole key loop.
+    // not keep 16*NT row positions alive across the whole key loop.  Row rho
+    // = base + o (o <= 27) is tail position rho mod n_eff; rows past R hold
+    // zero queries and a +inf bias, so their terms are 0 whatever ti is.
     int base;
     asm volatile("v_mov_b32 %0, %1" : "=v"(base) : "v"(row0 + t * 32 + 4 * (lane >> 5)));
+    if (n_eff >= 32) {
+      // one modulo per tile; base % n_eff + o < 2 n_eff needs one subtraction
+      const int tb = base % n_eff;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rho = base + 8 * (v >> 2) + (v & 3);
-      const int ti = rho < R ? rho % n_eff : 0;
-      if (!((key < key1) && (key <= qpos0 + ti))) e[v] = 0.f;
+      for (int v = 0; v < 16; ++v) {
+        int ti = tb + 8 * (v >> 2) + (v & 3);
+        ti = ti >= n_eff ? ti - n_eff : ti;
+        if (!((key < key1) && (key <= qpos0 + ti))) e[v] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ti = (base + 8 * (v >> 2) + (v & 3)) % n_eff;
+        if (!((key < key1) && (key <= qpos0 + ti))) e[v] = 0.f;
+      }
     }
   }
   return tree_sum16(e);
@@ -704,7 +725,7 @@ __device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t*
         f32x16_t sacc = {};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) sacc = mfma32(qf[t][s], kf[s], sacc);
-        col += colsum_update<NT>(sacc, t, MASKED, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
+        col += colsum_update<NT>(sacc, t, MASKED, key, key1, lane, row0, n_eff, qpos0, C, bv);
       }
       col = sum_halves(col);
       colrow[wave][nt * 32 + (lane & 31)] = col;  // both halves hold the same sum
@@ -727,7 +748,7 @@ __device__ __forceinline__ void colsum_iter(const uint16_t* cur, const uint16_t*
       for (int s = 0; s < D / 16; ++s) nacc = mfma32(qf[0][s], kf[s], nacc);
     }
     const int key = tkey0 + nt * 32 + (lane & 31);
-    col += colsum_update<NT>(acc, t, MASKED, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
+    col += colsum_update<NT>(acc, t, MASKED, key, key1, lane, row0, n_eff, qpos0, C, bv);
     if (t == NT - 1) {
       col = sum_halves(col);
       colrow[wave][nt * 32 + (lane & 31)] = col;  // both halves hold the same sum
@@ -773,7 +794,7 @@ __device__ __forceinline__ void colsum_iter_db(const uint16_t* cur, const uint16
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) nacc = mfma32(qf[t1][s], kf[nt1 & 1][s], nacc);
     const int key = tkey0 + nt * 32 + (lane & 31);
-    col += colsum_update<NT>(acc, t, false, key, key1, lane, row0, R, n_eff, qpos0, C, bv);
+    col += colsum_update<NT>(acc, t, false, key, key1, lane, row0, n_eff, qpos0, C, bv);
     if (t == NT - 1) {
       col = sum_halves(col);
       colrow[wave][nt * 32 + (lane & 31)] = col;  // both halves hold the same sum
@@ -919,6 +940,13 @@ up_colsum_kernel(ScoreArgs a, SelectArgs sa) {
   const int qpos0 = L - n_eff;
   const float C = a.c;
 
+  // the first K tiles travel together with the query rows and the statistics
+  const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
+  const int ntiles = (key1 - key0 + KT - 1) / KT;
+  KStream<D, W> ks;
+  ks.init(kbase, a.k_tok, key0, key1, wave, lane);
+  ring_issue<RING>(ks, ntiles, kl);
+
   bf16x8_t qf[NT][D / 16];
   int ipos_unused[NT];
   load_q<D, NT>(a, s0, qpos0, n_eff, R, g, row0, lane, qf, ipos_unused);
@@ -984,18 +1012,14 @@ up_colsum_kernel(ScoreArgs a, SelectArgs sa) {
       bv[t][v] = sbias[row0 - wg_row0 + t * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)];
   }
 
-  const uint16_t* kbase = a.k + (int64_t)s0 * a.k_tok + (int64_t)g * a.k_head;
   float* colout = a.colpart + ((int64_t)g * a.rg + rgi) * a.T + s0;
-  const int ntiles = (key1 - key0 + KT - 1) / KT;
   const int lim = min(key1, qpos0 + 1);
   const int nfast = lim > key0 ? (lim - key0) / KT : 0;
   constexpr bool DB = PIPE && (KT / 32) % 2 == 0;  // double-buffered fragments
   bf16x8_t kfb[DB ? 2 : 1][D / 16];
   auto& kf = kfb[0];
   int it = 0;
-  KStream<D, W> ks;
-  ks.init(kbase, a.k_tok, key0, key1, wave, lane);
-  ring_prologue<RING>(ks, ntiles, kl);
+  ring_ready<RING, Tile>(ntiles);
 
   // Loop structure as in pass A: steady state with whole-tile prefetch and
   // a fixed wait, then the last mask-free tiles, then the masked tiles.
