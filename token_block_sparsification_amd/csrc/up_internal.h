@@ -42,6 +42,9 @@ struct ScoreGeometry {
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv,
                              int head_dim, int n_query);
 
+// Workgroups of a scoring pass (pass_b: the column-sum pass) resident at once.
+int resident_wgs_for(int head_dim, bool pass_b);
+
 // Number of blocks a compaction tile spans for block size G.
 int compact_tile_blocks(int block);
 

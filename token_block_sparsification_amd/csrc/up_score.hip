@@ -1217,6 +1217,22 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, int ck_b, int64_t gro
 
 }  // namespace
 
+// Workgroups of one pass resident on the chip at once: both passes run two
+// waves per SIMD (their register budgets), i.e. 8 waves per CU, W waves per
+// workgroup, on the UP_NUM_CUS CUs of gfx950.
+#ifndef UP_NUM_CUS
+#define UP_NUM_CUS 256
+#endif
+int resident_wgs_for(int d, bool pass_b) {
+  int w;
+  switch (d) {
+    case 64: w = pass_b ? Tiling<64>::B::W : Tiling<64>::A::W; break;
+    case 128: w = pass_b ? Tiling<128>::B::W : Tiling<128>::A::W; break;
+    default: w = pass_b ? Tiling<256>::B::W : Tiling<256>::A::W; break;
+  }
+  return UP_NUM_CUS * std::max(1, 8 / w);
+}
+
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv, int head_dim,
                              int n_query) {
   ScoreGeometry g{};
@@ -1240,26 +1256,21 @@ extern "C" up_status up_score_workspace_size(int num_seqs, const int32_t* cu_seq
 
 namespace {
 
-#ifndef UP_MIN_WGS
-#define UP_MIN_WGS 512
-#endif
 #ifndef UP_CK_OVERHEAD
 #define UP_CK_OVERHEAD 256
 #endif
-// Key chunk per workgroup: the largest power of two in [256, UP_CK_MAX] that
-// still gives >= UP_MIN_WGS workgroups for this batch.  512 is one resident
-// round on the 256 CUs of gfx950 (two row-statistics workgroups per CU, and
-// half as many column-sum workgroups at one per CU): longer chunks cost less
-// per key (ring fill, Q loads, chunk merges) as long as every CU has work.
-// Measured against 2048-key chunks with >= 1024 workgroups: 15% less
-// scoring time at L = 32K, 3% less at 128K.
-int choose_ck(int num_seqs, const int32_t* cu_h, int hkv, int rg) {
+// Row-statistics key chunk: the largest power of two in [256, UP_CK_MAX]
+// that still gives one resident round of workgroups (`resident`, at least)
+// for this batch: longer chunks cost less per key (ring fill, Q loads, chunk
+// merges) as long as every CU has work.  Measured against 2048-key chunks
+// with two rounds: 15% less scoring time at L = 32K, 3% less at 128K.
+int choose_ck(int num_seqs, const int32_t* cu_h, int hkv, int rg_a, int resident) {
   int ck = UP_CK_MAX;
   while (ck > 256) {
     int64_t wgs = 0;
     for (int r = 0; r < num_seqs; ++r)
-      wgs += up::ceil_div(cu_h[r + 1] - cu_h[r], ck) * (int64_t)hkv * rg;
-    if (wgs >= UP_MIN_WGS) break;
+      wgs += up::ceil_div(cu_h[r + 1] - cu_h[r], ck) * (int64_t)hkv * rg_a;
+    if (wgs >= resident) break;
     ck >>= 1;
   }
   return ck;
@@ -1269,15 +1280,16 @@ int choose_ck(int num_seqs, const int32_t* cu_h, int hkv, int rg) {
 // a batch all take about the same time per key, so a last round that only
 // part fills the chip costs as much as a full one: pick the chunk (a multiple
 // of 64 keys, at most UP_CK_MAX) that minimises rounds x (chunk + per-workgroup
-// overhead), where one round holds UP_MIN_WGS / (hkv * rg) chunks (two
-// workgroups per CU on 256 CUs for the row groups of one KV head).  Single
-// requests keep the chunk of the rule above; a 16-request batch of 542K
-// tokens gets 2944-key chunks in 6 rounds instead of 4096-key chunks in 5,
-// the last one part full (column sums 657 vs 698 us).  Past 4096 requests the
-// search is skipped.
-int choose_ck_rounds(int num_seqs, const int32_t* cu_h, int hkv, int rg, int fallback) {
+// overhead), where one round holds resident / (hkv * rg) chunks (the
+// column-sum workgroups resident at once, over the row groups of one KV
+// head).  Single requests keep the chunk of the rule above; a 16-request
+// batch of 542K tokens gets 2944-key chunks in 6 rounds instead of 4096-key
+// chunks in 5, the last one part full (column sums 657 vs 698 us).  Past 4096
+// requests the search is skipped.
+int choose_ck_rounds(int num_seqs, const int32_t* cu_h, int hkv, int rg, int resident,
+                     int fallback) {
   if (num_seqs > 4096) return fallback;
-  const int64_t per_round = std::max<int64_t>(1, UP_MIN_WGS / ((int64_t)hkv * rg));
+  const int64_t per_round = std::max<int64_t>(1, resident / ((int64_t)hkv * rg));
   int best_ck = fallback;
   int64_t best = INT64_MAX;
   for (int ck = 256; ck <= UP_CK_MAX; ck += 64) {
@@ -1311,8 +1323,8 @@ up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int h
   if (n_query < 1 || n_query > 4096)
     return up::set_error(UP_ERR_UNSUPPORTED, "n_query %d not in [1, 4096]", n_query);
   up::ScoreGeometry g = up::score_geometry(num_seqs, T, max_len, hq, hkv, head_dim, n_query);
-  g.ck = choose_ck(num_seqs, cu_h, hkv, g.rg > g.rg_a ? g.rg : g.rg_a);
-  g.ck_b = choose_ck_rounds(num_seqs, cu_h, hkv, g.rg > g.rg_a ? g.rg : g.rg_a, g.ck);
+  g.ck = choose_ck(num_seqs, cu_h, hkv, g.rg_a, up::resident_wgs_for(head_dim, false));
+  g.ck_b = choose_ck_rounds(num_seqs, cu_h, hkv, g.rg, up::resident_wgs_for(head_dim, true), g.ck);
   g.max_chunks = (int)(max_len > 0 ? up::ceil_div(max_len, g.ck) : 1);
   size_t off = 0;
   g.off_partial = off;
