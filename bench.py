@@ -95,7 +95,7 @@ TRAFFIC_KERNELS = {
     "up_compact_scan_kernel": ("up_compact.hip", r"\bup_compact_scan_kernel\b"),
     "up_rowstats_kernel": ("up_score.hip", r"\bup_rowstats_kernel\b"),
     "up_colsum_kernel": ("up_score.hip", r"\bup_colsum_kernel\b"),
-    "up_select_kernel": (("up_select.hip", "up_select_impl.h"), r"\bup_select_kernel\b"),
+    "up_select_kernel": (("up_select.hip", "up_select_impl.h", "up_wave.h"), r"\bup_select_kernel\b"),
     "up_rowop_kernel_norm": ("up_compact.hip", r"\bup_rowop_kernel<0, "),
     "up_rowop_kernel_add": ("up_compact.hip", r"\bup_rowop_kernel<1, "),
 }

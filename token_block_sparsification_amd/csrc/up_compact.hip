@@ -33,6 +33,7 @@
 #include <mutex>
 
 #include "up_internal.h"
+#include "up_wave.h"
 
 namespace up {
 namespace {
@@ -183,12 +184,7 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
       }
     }
     // Exclusive scan of the threads' kept rows: waves, then across waves.
-    int64_t incl = mine;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int64_t y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
+    const int64_t incl = (int64_t)wave_scan_incl((uint64_t)mine);
     if (lane == 63) s_wave[wave] = incl;
     __syncthreads();
     int64_t wbase = 0, agg = 0;
@@ -227,10 +223,8 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
           // a predecessor that never published counts as 0 rows: the
           // offsets are wrong, so the call's status records it
           if (lane <= stop && state == 0) atomicOr(&a.ctl[2], kStatusLookbackGaveUp);
-          int64_t v = (lane <= stop && state != 0) ? (int64_t)(f & kValueMask) : 0;
-#pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-          excl += v;
+          const uint64_t v = (lane <= stop && state != 0) ? (f & kValueMask) : 0;
+          excl += (int64_t)wave_sum(v);
           if (incl_lanes) break;
           hi -= 64;
         }

@@ -897,8 +897,7 @@ __device__ void chunk_scores(const ScoreArgs& a, int req, int s0, int key0, int 
     const int j0 = i * G, j1 = min(j0 + G, nk);
     float sum = 0.f;
     for (int j = j0 + lane; j < j1; j += 64) sum += cs[j];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    sum = wave_sum_f32(sum);
     if (lane == 0) store_coherent(&a.block_scores[b0 + i], sum / (float)(j1 - j0));
   }
 }
@@ -1134,8 +1133,7 @@ __device__ __forceinline__ void blockmean_one(const ScoreArgs& a, int64_t b, int
     if (a.token_scores) a.token_scores[s0 + j] = c;
     sum += c;
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  sum = wave_sum_f32(sum);
   if (lane == 0) a.block_scores[b] = sum / (float)(j1 - j0);
 }
 
