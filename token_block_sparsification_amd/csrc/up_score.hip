@@ -457,11 +457,13 @@ __device__ __forceinline__ void rowstats_update(f32x16_t acc, int t, bool masked
 #pragma unroll
   for (int v = 0; v < 16; ++v) x[v] = acc[v];
   if (masked) {
+    // key j = mkey0 + 4 (lane / 32) + o_v with o_v = 8 (v / 4) + v % 4 (a
+    // constant): valid iff j < key1 and j <= the row's position, i.e. o_v
+    // <= thr; one compare per element
+    const int thr = min(key1 - 1, ipos[t]) - (mkey0 + 4 * (lane >> 5));
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int j = mkey0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (j >= key1 || j > ipos[t]) x[v] = kNegInf;
-    }
+    for (int v = 0; v < 16; ++v)
+      if (8 * (v >> 2) + (v & 3) > thr) x[v] = kNegInf;
   }
   float mx = fmaxf(fmaxf(x[0], x[1]), m_run[t]);
 #pragma unroll
@@ -682,7 +684,17 @@ __device__ __forceinline__ float colsum_update(f32x16_t acc, int t, bool masked,
     // zero queries and a +inf bias, so their terms are 0 whatever ti is.
     int base;
     asm volatile("v_mov_b32 %0, %1" : "=v"(base) : "v"(row0 + t * 32 + 4 * (lane >> 5)));
-    if (n_eff >= 32) {
+    if (n_eff % 32 == 0) {
+      // 32-row tiles never straddle two heads' rows: row base + o_v (o_v =
+      // 8 (v / 4) + v % 4, a constant) is tail position tb + o_v, and the key
+      // is valid for it iff key < key1 and key <= qpos0 + tb + o_v, i.e.
+      // o_v >= thr; one compare per element
+      const int tb = base % n_eff;
+      const int thr = key < key1 ? key - qpos0 - tb : (1 << 30);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (8 * (v >> 2) + (v & 3) < thr) e[v] = 0.f;
+    } else if (n_eff >= 32) {
       // one modulo per tile; base % n_eff + o < 2 n_eff needs one subtraction
       const int tb = base % n_eff;
 #pragma unroll
