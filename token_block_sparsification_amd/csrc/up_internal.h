@@ -31,7 +31,9 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct ScoreGeometry {
   int rows_per_wg;   // query rows one column-sum workgroup holds in registers
   int rg;            // column-sum row groups per KV head
-  int rg_a;          // row-statistics row groups per KV head
+  int rg_a;          // row-statistics row groups per KV head (of the tiling in use)
+  int rg_a1;         // the same for pass A's one-round tiling
+  int one_round_a;   // pass A runs its one-round tiling
   int ck;            // keys per row-statistics workgroup chunk (sets the partials layout)
   int ck_b;          // keys per column-sum workgroup chunk
   int max_chunks;    // chunks of the longest request
@@ -42,8 +44,10 @@ struct ScoreGeometry {
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv,
                              int head_dim, int n_query);
 
-// Workgroups of a scoring pass (pass_b: the column-sum pass) resident at once.
-int resident_wgs_for(int head_dim, bool pass_b);
+// Workgroups of a scoring pass resident at once (pass 0: row statistics,
+// 1: row statistics in its one-round tiling, 2: column sums).
+int resident_wgs_for(int head_dim, int pass);
+bool has_one_round_tiling(int head_dim);
 
 // Number of blocks a compaction tile spans for block size G.
 int compact_tile_blocks(int block);

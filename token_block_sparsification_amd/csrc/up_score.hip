@@ -1174,6 +1174,16 @@ __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
 #ifndef UP_TILE_A256
 #define UP_TILE_A256 1, 4, true, 4
 #endif
+// Pass A at head_dim 128 when the whole batch fits one resident round: one
+// 8-wave workgroup per CU.  Two 4-wave workgroups sharing a CU drift apart
+// (the SIMD arbiter prefers the older one's waves), and with no further
+// round to fill in, the younger one ends the pass alone at one wave per SIMD
+// (128K: 141 vs 146 us); over several rounds the two-workgroup form wins
+// (the 16-request batch: 595 vs 644 us), since one workgroup's prologue
+// overlaps the other's key loop.
+#ifndef UP_TILE_A128_ONE_ROUND
+#define UP_TILE_A128_ONE_ROUND 2, 8, true, 4
+#endif
 #ifndef UP_TILE_B256
 #define UP_TILE_B256 1, 4, true, 4
 #endif
@@ -1184,32 +1194,66 @@ struct TileCfg {
   static constexpr int ROWS = NT * 32 * W;
 };
 template <int D> struct Tiling;
-template <> struct Tiling<64> { using A = TileCfg<UP_TILE_A64>; using B = TileCfg<UP_TILE_B64>; };
-template <> struct Tiling<128> { using A = TileCfg<UP_TILE_A128>; using B = TileCfg<UP_TILE_B128>; };
-template <> struct Tiling<256> { using A = TileCfg<UP_TILE_A256>; using B = TileCfg<UP_TILE_B256>; };
+// A1: the pass-A tiling for a batch that fits one resident round of it.
+template <> struct Tiling<64> {
+  using A = TileCfg<UP_TILE_A64>;
+  using A1 = A;
+  using B = TileCfg<UP_TILE_B64>;
+};
+template <> struct Tiling<128> {
+  using A = TileCfg<UP_TILE_A128>;
+  using A1 = TileCfg<UP_TILE_A128_ONE_ROUND>;
+  using B = TileCfg<UP_TILE_B128>;
+};
+template <> struct Tiling<256> {
+  using A = TileCfg<UP_TILE_A256>;
+  using A1 = A;
+  using B = TileCfg<UP_TILE_B256>;
+};
 
-int rows_per_wg_for(int d, bool pass_b) {
+// Rows and waves per workgroup of pass A (pass 0), pass A's one-round
+// tiling (pass 1) and pass B (pass 2).
+template <typename T>
+int tiling_rows(int pass) {
+  return pass == 0 ? T::A::ROWS : pass == 1 ? T::A1::ROWS : T::B::ROWS;
+}
+template <typename T>
+int tiling_waves(int pass) {
+  return pass == 0 ? T::A::W : pass == 1 ? T::A1::W : T::B::W;
+}
+int rows_per_wg_for(int d, int pass) {
   switch (d) {
-    case 64: return pass_b ? Tiling<64>::B::ROWS : Tiling<64>::A::ROWS;
-    case 128: return pass_b ? Tiling<128>::B::ROWS : Tiling<128>::A::ROWS;
-    default: return pass_b ? Tiling<256>::B::ROWS : Tiling<256>::A::ROWS;
+    case 64: return tiling_rows<Tiling<64>>(pass);
+    case 128: return tiling_rows<Tiling<128>>(pass);
+    default: return tiling_rows<Tiling<256>>(pass);
+  }
+}
+int waves_per_wg_for(int d, int pass) {
+  switch (d) {
+    case 64: return tiling_waves<Tiling<64>>(pass);
+    case 128: return tiling_waves<Tiling<128>>(pass);
+    default: return tiling_waves<Tiling<256>>(pass);
   }
 }
 
 int64_t grid_for(const ScoreArgs& a) { return ceil_div(a.num_groups, 8) * 8 * a.rg; }
 
-template <int D>
-up_status launch_passes(const ScoreArgs& b_args, int rg_a, int ck_b, int64_t groups_b,
-                        const SelectArgs* sel, hipStream_t st) {
-  using TA = typename Tiling<D>::A;
-  using TB = typename Tiling<D>::B;
+template <int D, typename TA>
+up_status launch_rowstats(const ScoreArgs& b_args, int rg_a, hipStream_t st) {
   ScoreArgs aa = b_args;
   aa.rg = rg_a;
   aa.rows_per_wg = TA::ROWS;
   hipLaunchKernelGGL((up_rowstats_kernel<D, TA::NT, TA::W, TA::PIPE, TA::RING>),
-                     dim3((unsigned)grid_for(aa)),
-                     dim3(64 * TA::W), 0, st, aa);
-  up_status s = check_launch("up_rowstats_kernel");
+                     dim3((unsigned)grid_for(aa)), dim3(64 * TA::W), 0, st, aa);
+  return check_launch("up_rowstats_kernel");
+}
+
+template <int D>
+up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int ck_b,
+                        int64_t groups_b, const SelectArgs* sel, hipStream_t st) {
+  using TB = typename Tiling<D>::B;
+  up_status s = one_round_a ? launch_rowstats<D, typename Tiling<D>::A1>(b_args, rg_a, st)
+                            : launch_rowstats<D, typename Tiling<D>::A>(b_args, rg_a, st);
   if (s != UP_OK) return s;
   ScoreArgs bb = b_args;  // the column-sum pass chunks the keys its own way
   bb.ck_a = b_args.ck;
@@ -1233,14 +1277,12 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, int ck_b, int64_t gro
 #ifndef UP_NUM_CUS
 #define UP_NUM_CUS 256
 #endif
-int resident_wgs_for(int d, bool pass_b) {
-  int w;
-  switch (d) {
-    case 64: w = pass_b ? Tiling<64>::B::W : Tiling<64>::A::W; break;
-    case 128: w = pass_b ? Tiling<128>::B::W : Tiling<128>::A::W; break;
-    default: w = pass_b ? Tiling<256>::B::W : Tiling<256>::A::W; break;
-  }
-  return UP_NUM_CUS * std::max(1, 8 / w);
+int resident_wgs_for(int d, int pass) {
+  return UP_NUM_CUS * std::max(1, 8 / waves_per_wg_for(d, pass));
+}
+
+bool has_one_round_tiling(int d) {
+  return d == 128 && !std::is_same<Tiling<128>::A, Tiling<128>::A1>::value;
 }
 
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv, int head_dim,
@@ -1248,10 +1290,13 @@ ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int h
   ScoreGeometry g{};
   const int rgqa = hkv > 0 ? hq / hkv : 1;
   const int64_t rmax = (int64_t)rgqa * (n_query < max_len ? n_query : max_len);
-  g.rows_per_wg = rows_per_wg_for(head_dim, true);
+  g.rows_per_wg = rows_per_wg_for(head_dim, 2);
   g.rg = (int)(rmax > 0 ? ceil_div(rmax, g.rows_per_wg) : 1);
-  const int rows_a = rows_per_wg_for(head_dim, false);
+  const int rows_a = rows_per_wg_for(head_dim, 0);
   g.rg_a = (int)(rmax > 0 ? ceil_div(rmax, rows_a) : 1);
+  const int rows_a1 = rows_per_wg_for(head_dim, 1);
+  g.rg_a1 = (int)(rmax > 0 ? ceil_div(rmax, rows_a1) : 1);
+  g.one_round_a = 0;
   g.ck = 0;  // chosen by the caller once lengths are known
   g.max_chunks = 0;
   (void)num_seqs;
@@ -1333,8 +1378,21 @@ up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int h
   if (n_query < 1 || n_query > 4096)
     return up::set_error(UP_ERR_UNSUPPORTED, "n_query %d not in [1, 4096]", n_query);
   up::ScoreGeometry g = up::score_geometry(num_seqs, T, max_len, hq, hkv, head_dim, n_query);
-  g.ck = choose_ck(num_seqs, cu_h, hkv, g.rg_a, up::resident_wgs_for(head_dim, false));
-  g.ck_b = choose_ck_rounds(num_seqs, cu_h, hkv, g.rg, up::resident_wgs_for(head_dim, true), g.ck);
+  g.ck = choose_ck(num_seqs, cu_h, hkv, g.rg_a, up::resident_wgs_for(head_dim, 0));
+  if (up::has_one_round_tiling(head_dim)) {
+    // pass A's one-round tiling when its chunk rule gives at most one round
+    const int res1 = up::resident_wgs_for(head_dim, 1);
+    const int ck1 = choose_ck(num_seqs, cu_h, hkv, g.rg_a1, res1);
+    int64_t wgs1 = 0;
+    for (int r = 0; r < num_seqs; ++r)
+      wgs1 += up::ceil_div(cu_h[r + 1] - cu_h[r], ck1) * (int64_t)hkv * g.rg_a1;
+    if (wgs1 <= res1) {
+      g.one_round_a = 1;
+      g.rg_a = g.rg_a1;
+      g.ck = ck1;
+    }
+  }
+  g.ck_b = choose_ck_rounds(num_seqs, cu_h, hkv, g.rg, up::resident_wgs_for(head_dim, 2), g.ck);
   g.max_chunks = (int)(max_len > 0 ? up::ceil_div(max_len, g.ck) : 1);
   size_t off = 0;
   g.off_partial = off;
@@ -1489,9 +1547,15 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
                         sel->kept_tokens, block, sel->sink, sel->tail, sel->top_p};
   const up::SelectArgs* sap = sel ? &sa : nullptr;
   switch (head_dim) {
-    case 64: st = up::launch_passes<64>(a, lay.g.rg_a, ck_b, groups_b, sap, stream); break;
-    case 128: st = up::launch_passes<128>(a, lay.g.rg_a, ck_b, groups_b, sap, stream); break;
-    default: st = up::launch_passes<256>(a, lay.g.rg_a, ck_b, groups_b, sap, stream); break;
+    case 64:
+      st = up::launch_passes<64>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, sap, stream);
+      break;
+    case 128:
+      st = up::launch_passes<128>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, sap, stream);
+      break;
+    default:
+      st = up::launch_passes<256>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, sap, stream);
+      break;
   }
   if (st != UP_OK || sel) return st;
   hipLaunchKernelGGL(up::up_blockmean_kernel, dim3((unsigned)up::ceil_div(N, 4)), dim3(256), 0,
