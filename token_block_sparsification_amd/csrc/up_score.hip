@@ -372,13 +372,13 @@ __device__ __forceinline__ void load_q(const ScoreArgs& a, int s0, int qpos0, in
 // ---------------------------------------------------------------------------
 // Shared pieces of the two passes.
 //
-// Both passes walk the chunk's keys in LDS tiles of KT keys held in a
-// four-buffer ring: when iteration it starts, tiles it and it+1 are resident
-// and tile it+2 is in flight; iteration it fetches tile it+3.  Both passes
-// may software-pipeline over "groups": one
-// group is one 32x32 S tile (32 keys x 32 query rows).  While the VALU works
-// on group g (scale, exp2, reductions), the MFMAs of group g+1 are already
-// issued, so the matrix cores and the VALU run side by side within a wave.
+// Both passes walk the chunk's keys in LDS tiles of KT keys held in the
+// RING-slot ring above (tiles it and it+1 resident when iteration it starts,
+// RING-3 more in flight).  Both passes may software-pipeline over "groups":
+// one group is one 32x32 S tile (32 keys x 32 query rows).  While the VALU
+// works on group g (scale, exp2, reductions), the MFMAs of group g+1 are
+// already issued, so the matrix cores and the VALU run side by side within a
+// wave.
 // ---------------------------------------------------------------------------
 
 // Sum of 16 values as a balanced tree (short dependency chains).
