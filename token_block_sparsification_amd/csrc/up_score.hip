@@ -1174,15 +1174,23 @@ __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
 #ifndef UP_TILE_A256
 #define UP_TILE_A256 1, 4, true, 4
 #endif
-// Pass A at head_dim 128 when the whole batch fits one resident round: one
-// 8-wave workgroup per CU.  Two 4-wave workgroups sharing a CU drift apart
-// (the SIMD arbiter prefers the older one's waves), and with no further
-// round to fill in, the younger one ends the pass alone at one wave per SIMD
-// (128K: 141 vs 146 us); over several rounds the two-workgroup form wins
-// (the 16-request batch: 595 vs 644 us), since one workgroup's prologue
-// overlaps the other's key loop.
+// Pass A when the whole batch fits one resident round: one 8-wave workgroup
+// per CU.  Two 4-wave workgroups sharing a CU drift apart (the SIMD arbiter
+// prefers the older one's waves), and with no further round to fill in, the
+// younger one ends the pass alone at one wave per SIMD (scoring at 128K,
+// head_dim 128: row statistics 141 vs 146 us; head_dim 256, n = 128: 300 vs
+// 316 us per call); over several rounds the two-workgroup form wins (the
+// 16-request batch: 595 vs 644 us), since one workgroup's prologue overlaps
+// the other's key loop.  At head_dim 64 the 8-wave form measured slower
+// (2K tokens: 25.7 vs 23.7 us per call), so there it is not used.
 #ifndef UP_TILE_A128_ONE_ROUND
 #define UP_TILE_A128_ONE_ROUND 2, 8, true, 4
+#endif
+#ifndef UP_TILE_A256_ONE_ROUND
+#define UP_TILE_A256_ONE_ROUND 1, 8, true, 4
+#endif
+#ifndef UP_TILE_A64_ONE_ROUND
+#define UP_TILE_A64_ONE_ROUND UP_TILE_A64
 #endif
 #ifndef UP_TILE_B256
 #define UP_TILE_B256 1, 4, true, 4
@@ -1197,7 +1205,7 @@ template <int D> struct Tiling;
 // A1: the pass-A tiling for a batch that fits one resident round of it.
 template <> struct Tiling<64> {
   using A = TileCfg<UP_TILE_A64>;
-  using A1 = A;
+  using A1 = TileCfg<UP_TILE_A64_ONE_ROUND>;
   using B = TileCfg<UP_TILE_B64>;
 };
 template <> struct Tiling<128> {
@@ -1207,7 +1215,7 @@ template <> struct Tiling<128> {
 };
 template <> struct Tiling<256> {
   using A = TileCfg<UP_TILE_A256>;
-  using A1 = A;
+  using A1 = TileCfg<UP_TILE_A256_ONE_ROUND>;
   using B = TileCfg<UP_TILE_B256>;
 };
 
@@ -1282,7 +1290,11 @@ int resident_wgs_for(int d, int pass) {
 }
 
 bool has_one_round_tiling(int d) {
-  return d == 128 && !std::is_same<Tiling<128>::A, Tiling<128>::A1>::value;
+  switch (d) {
+    case 64: return !std::is_same<Tiling<64>::A, Tiling<64>::A1>::value;
+    case 128: return !std::is_same<Tiling<128>::A, Tiling<128>::A1>::value;
+    default: return !std::is_same<Tiling<256>::A, Tiling<256>::A1>::value;
+  }
 }
 
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv, int head_dim,
