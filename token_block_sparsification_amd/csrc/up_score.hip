@@ -1193,7 +1193,7 @@ __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
 #define UP_TILE_A64_ONE_ROUND UP_TILE_A64
 #endif
 #ifndef UP_TILE_B256
-#define UP_TILE_B256 1, 4, true, 4
+#define UP_TILE_B256 1, 8, true, 4
 #endif
 template <int NT_, int W_, bool PIPE_, int RING_>
 struct TileCfg {
