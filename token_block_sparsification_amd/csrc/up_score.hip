@@ -1279,14 +1279,15 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int
 
 }  // namespace
 
-// Workgroups of one pass resident on the chip at once: both passes run two
-// waves per SIMD (their register budgets), i.e. 8 waves per CU, W waves per
-// workgroup, on the UP_NUM_CUS CUs of gfx950.
+// Workgroups of one pass resident on the chip at once: a pass runs the waves
+// per SIMD its register budget allows (UP_OCC_A / UP_OCC_B, so 4 times that
+// per CU), W waves per workgroup, on the UP_NUM_CUS CUs of gfx950.
 #ifndef UP_NUM_CUS
 #define UP_NUM_CUS 256
 #endif
 int resident_wgs_for(int d, int pass) {
-  return UP_NUM_CUS * std::max(1, 8 / waves_per_wg_for(d, pass));
+  const int waves_per_cu = 4 * (pass == 2 ? UP_OCC_B : UP_OCC_A);
+  return UP_NUM_CUS * std::max(1, waves_per_cu / waves_per_wg_for(d, pass));
 }
 
 bool has_one_round_tiling(int d) {
