@@ -3,7 +3,8 @@
 
 A step is the whole hot path over one packed batch already resident in HBM:
 up_score (tail-query scores + block means) -> up_select_topp (Top-p mask) ->
-up_compact (gather of kept rows) -> up_drop_history (ledger append).
+up_compact_record (gather of kept rows, and the ledger append in the same
+copy launch: up_compact + up_drop_history in one call).
 
 Default workload: Llama-3.1-8B-shaped full-attention layer, one request of
 L = 131072 tokens, 32 q / 8 KV heads, head_dim 128, hidden 4096 bf16, n=128,
@@ -186,7 +187,7 @@ def main():
     U.up_history_init(ledger, batch.num_seqs, cap)
     T, N, B = batch.num_tokens, batch.num_blocks, batch.num_seqs
 
-    calls = ["up_score", "up_select_topp", "up_compact", "up_drop_history"]
+    calls = ["up_score", "up_select_topp", "up_compact_record"]
 
     def step(layer=0, marks=None):
         """One pass of the path.  marks: {call: (start, end) HIP events} for
@@ -204,11 +205,10 @@ def main():
         run("up_select_topp", lambda: U.up_select_topp(
             batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, ws.block_scores, w.block,
             w.top_p, w.sink, w.tail, ws.block_mask, ws.kept_tokens))
-        run("up_compact", lambda: U.up_compact(
+        run("up_compact_record", lambda: U.up_compact_record(
             batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, w.block, ws.block_mask,
-            hidden, pos, ws.hidden_out, ws.positions_out, ws.cu_seqlens_out, ws.compact_ws))
-        run("up_drop_history", lambda: U.up_drop_history(ledger, B, cap, layer % cap,
-                                                         ws.cu_seqlens_out))
+            hidden, pos, ws.hidden_out, ws.positions_out, ws.cu_seqlens_out, ws.compact_ws,
+            ledger, cap, layer % cap))
 
     def new_marks(names):
         return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -240,12 +240,12 @@ def main():
     kept = int(ws.cu_seqlens_out[-1].item())
 
     # Timed region: K steps; on every EVENT_EVERY-th step the two large calls
-    # (up_score, up_compact) are bracketed by events, and the larger of them
+    # (up_score, up_compact_record) are bracketed by events, and the larger of them
     # over the timed region is the dominant one.  Each event record leaves
     # the GPU idle for ~5 us, so bracketing every step would add ~11 us per
     # call bracketed.
     K = args.steps
-    big = ("up_score", "up_compact")
+    big = ("up_score", "up_compact_record")
     sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
     timed_marks = {i: new_marks(list(big)) for i in sampled}
     U.up_history_init(ledger, B, cap)
@@ -384,16 +384,16 @@ def main():
     score_bytes = T * w.hkv * w.head_dim * 2 + sum(min(w.n_query, L) for L in lens) * w.hq * w.head_dim * 2
 
     t_score = per_call_us["up_score"] * 1e-6
-    t_compact = per_call_us["up_compact"] * 1e-6
+    t_compact = per_call_us["up_compact_record"] * 1e-6
     t_select = per_call_us["up_select_topp"] * 1e-6
     compact_gbs = compact_bytes / t_compact / 1e9
     score_tflops_exec = flops_exec / t_score / 1e12
     score_tflops_alg = flops_alg / t_score / 1e12
 
-    if dominant == "up_compact":
+    if dominant == "up_compact_record":
         # The copy kernel moves every byte; the events bracket the whole
-        # up_compact call (its small scan launch included), so `achieved`
-        # slightly understates the copy kernel's own rate.
+        # up_compact_record call (its small scan launch included), so
+        # `achieved` slightly understates the copy kernel's own rate.
         tc = load_traffic("up_compact_copy_kernel", "up_compact.hip", w.name)
         ts = load_traffic("up_compact_scan_kernel", "up_compact.hip", w.name)
         traffic = tc + ts if tc is not None and ts is not None else None
@@ -401,7 +401,7 @@ def main():
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
                     "traffic": traffic,
                     "algorithmic_bytes_per_launch": int(compact_bytes),
-                    "duration": ("HIP events around up_compact (scan + copy launches) on every "
+                    "duration": ("HIP events around up_compact_record (scan + copy launches) on every "
                                  f"{EVENT_EVERY}th step of the timed region ({len(dom_all)} launches)")}
     else:
         roofline = {"kernel": "up_score (rowstats+colsum+blockmean)", "bound": "mfma",
@@ -432,12 +432,12 @@ def main():
         "up_gather_add_gbs": gbs(add_bytes, fz_us["up_gather_add"]),
         "up_gather_add_frac_of_hbm_peak": round(gbs(add_bytes, fz_us["up_gather_add"]) / PEAK_HBM_GBS, 4),
         "up_gather_add_algorithmic_bytes": int(add_bytes),
-        "unfused_compact_then_torch_rmsnorm_us": round(per_call_us["up_compact"] + fz_us["torch_rmsnorm"], 2),
+        "unfused_compact_then_torch_rmsnorm_us": round(per_call_us["up_compact_record"] + fz_us["torch_rmsnorm"], 2),
         "chain_fused_us": round(fz_us["chain_fused"], 2),
         "chain_unfused_with_torch_rmsnorm_us": round(unfused_chain_us, 2),
         "note": ("chain_fused = up_score_select + up_compact_rmsnorm + up_drop_history (the "
                  "next layer's normalised operand produced from the frozen rows); the unfused "
-                 "chain adds torch's RMSNorm of the compacted rows to the four calls"),
+                 "chain adds torch's RMSNorm of the compacted rows to the step's calls"),
     }
 
     rec = {

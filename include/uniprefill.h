@@ -18,6 +18,7 @@
  *   up_revive       scatter of packed kept rows back into the full buffer
  * and, fused:
  *   up_score_select     up_score + up_select_topp, selecting in the column-sum kernel
+ *   up_compact_record   up_compact + up_drop_history, appending in the copy kernel
  * and, fused into the next layer's first reads (no compacted copy),
  *   up_compact_rmsnorm  normalised input operand of the kept rows
  *   up_gather_add       residual sum with the residual read from frozen rows
@@ -241,6 +242,27 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
                      void* hidden_out, int32_t* positions_out, int32_t* cu_seqlens_out,
                      int64_t out_capacity_rows, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/*
+ * up_compact_record — up_compact followed by up_drop_history in one call of
+ * two launches (§二 step 3 and §三: the compaction and its ledger entry, the
+ * metadata update of the same step).  Arguments: those of up_compact, then
+ * the ledger, its capacity and the layer id as for up_drop_history.  The
+ * copy kernel's first workgroup appends every request's (layer_id, kept
+ * tokens) entry from the cu_seqlens_out the scan wrote; a batch with no
+ * blocks appends through the ledger kernel instead.  Outputs (rows,
+ * positions, cu_seqlens_out, ledger words and status bits) are identical to
+ * up_compact then up_drop_history with the same arguments.
+ * ledger     device int32, as for up_drop_history (not NULL).
+ * capacity   >= 1 (UP_ERR_INVALID otherwise).
+ */
+up_status up_compact_record(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                            const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                            const void* hidden, int64_t row_bytes, int64_t row_stride_bytes,
+                            const int32_t* positions, void* hidden_out, int32_t* positions_out,
+                            int32_t* cu_seqlens_out, int64_t out_capacity_rows, void* workspace,
+                            size_t workspace_bytes, void* ledger, int capacity, int layer_id,
+                            hipStream_t stream);
 
 /*
  * up_compact_noalloc — up_compact without a caller workspace, for callers

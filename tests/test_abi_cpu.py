@@ -123,6 +123,22 @@ def test_compact_rejects_bad_arguments():
         assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())
 
 
+def test_compact_record_rejects_bad_arguments():
+    """up_compact's checks, plus the ledger's (NULL ledger, capacity < 1)."""
+    lib = U.lib()
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    base = [1, cu.data_ptr(), 16, 16, 64, 16, 4096, 512, 512, 4096, 8192, 8192, 16, 256, 256,
+            1 << 20, 4096, 4, 0, None]
+    cases = [((13, 255), 4, "capacity"), ((8, 256), 1, "row_stride"), ((7, 0), 1, "row_bytes"),
+             ((15, 16), 3, "workspace"), ((9, None), 1, "positions"), ((14, 300), 1, "256-byte"),
+             ((16, None), 1, "ledger"), ((17, 0), 1, "capacity >= 1")]
+    for (i, v), status, msg in cases:
+        a = list(base)
+        a[i] = v
+        st = lib.up_compact_record(*a)
+        assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())
+
+
 def test_history_rejects_bad_arguments():
     lib = U.lib()
     assert lib.up_history_init(None, 2, 4, None) == 1

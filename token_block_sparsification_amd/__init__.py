@@ -23,7 +23,7 @@ __all__ = [
     "up_abi_version", "up_last_error", "up_make_cu_blocks",
     "up_score_workspace_size", "up_score", "up_select_topp",
     "up_compact_workspace_size", "up_compact_workspace_init", "up_compact", "up_compact_status",
-    "up_compact_noalloc",
+    "up_compact_noalloc", "up_compact_record",
     "up_history_bytes", "up_history_init", "up_drop_history", "up_kv_len", "up_revive",
     "up_compact_rmsnorm", "up_gather_add", "up_score_select",
     "Batch", "Workspace", "run_chain",
@@ -69,6 +69,8 @@ _SIGNATURES = {
     "up_compact_workspace_init": (_I, [_P, _SZ, _P]),
     "up_compact": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P, _SZ,
                         _P]),
+    "up_compact_record": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P,
+                               _SZ, _P, _I, _I, _P]),
     "up_compact_status": (_I, [_P, _SZ, _P, _I, _P]),
     "up_compact_noalloc": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P,
                                 _P]),
@@ -247,6 +249,27 @@ def up_compact(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, 
                           hidden_out.shape[0], _ptr(workspace), workspace.numel(),
                           _stream(stream, hidden_out.device))
     _check("up_compact", st)
+
+
+def up_compact_record(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, hidden,
+                      positions, hidden_out, positions_out, cu_seqlens_out, workspace, ledger,
+                      capacity: int, layer_id: int, stream=None) -> None:
+    """up_compact, then the ledger append of up_drop_history, in two launches
+    (the copy kernel appends the entries)."""
+    if hidden.dim() < 1 or (hidden.dim() > 1 and not hidden[0].is_contiguous()):
+        raise ValueError("hidden rows must be contiguous")
+    if hidden_out.dtype != hidden.dtype:
+        raise ValueError("hidden_out must have hidden's dtype")
+    cu = _host_i32(cu_seqlens_h)
+    row_bytes = (hidden[0].numel() if hidden.dim() > 1 else 1) * hidden.element_size()
+    row_stride = hidden.stride(0) * hidden.element_size()
+    st = lib().up_compact_record(cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_d), _ptr(cu_blocks_d),
+                                 block, _ptr(block_mask), _ptr(hidden), row_bytes, row_stride,
+                                 _ptr(positions), _ptr(hidden_out), _ptr(positions_out),
+                                 _ptr(cu_seqlens_out), hidden_out.shape[0], _ptr(workspace),
+                                 workspace.numel(), _ptr(ledger), capacity, layer_id,
+                                 _stream(stream, hidden_out.device))
+    _check("up_compact_record", st)
 
 
 def up_compact_noalloc(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, block: int, block_mask, hidden,

@@ -26,7 +26,9 @@
 //     16-byte non-temporal loads and stores; dropped rows are never read.
 // Splitting the gather from the scan lets the copy use small, uniform work
 // items (the shape a plain device copy runs fastest with) instead of one
-// workgroup per scan tile.
+// workgroup per scan tile.  up_compact_record is up_compact whose copy kernel
+// also appends the ledger entries (workgroup 0, before its piece), so the
+// step needs no separate ledger launch.
 #include <math.h>
 
 #include <initializer_list>
@@ -108,6 +110,8 @@ struct CompactArgs {
   int64_t piece_bytes; // bytes per work item when rows are packed
   int64_t piece_rows;  // rows per work item when rows are strided
   int num_seqs, block;
+  int32_t* ledger;     // NULL, or the drop-history ledger the copy kernel appends to
+  int led_capacity, layer_id;
 };
 
 // Status bit of control word 2: a look-back gave up on a predecessor tile.
@@ -324,14 +328,44 @@ __device__ __forceinline__ void copy_rows(char* __restrict__ dst, int64_t dst_st
   }
 }
 
+// Drop-history ledger words: [0] status bits, [1] num_seqs, [2] capacity,
+// [3] reserved, then one entry count per request, then (layer id, kept
+// tokens) entries, capacity per request.
+constexpr int kLedgerHeader = 4;
+
+// Append (layer, kept tokens of request r) to request r's ledger record.  A
+// ledger set up for another shape gets status bit 1 (from r = 0), a full
+// record keeps its entries and sets bit 0.
+__device__ __forceinline__ void history_append_one(int32_t* led, int num_seqs, int capacity,
+                                                   int layer, const int32_t* cu_out, int r) {
+  if (led[1] != num_seqs || led[2] != capacity) {  // ledger set up for another shape
+    if (r == 0) atomicOr(&led[0], 2);
+    return;
+  }
+  const int cnt = led[kLedgerHeader + r];
+  const int kept = cu_out[r + 1] - cu_out[r];
+  if (cnt < capacity) {
+    int32_t* e = led + kLedgerHeader + num_seqs + 2 * ((int64_t)r * capacity + cnt);
+    e[0] = layer;
+    e[1] = kept;
+    led[kLedgerHeader + r] = cnt + 1;
+  } else {
+    atomicOr(&led[0], 1);
+  }
+}
+
 // Work item w = (block w / pieces, piece w % pieces): consecutive workgroups
 // copy consecutive pieces of one block, so the streams stay sequential in
-// memory.  A grid-stride loop covers batches with more items than one grid.
+// memory.  With a ledger, workgroup 0 first appends every request's entry
+// from cu_seqlens_out (written by the scan, the launch before).  A grid-stride loop covers batches with more items than one grid.
 // REVIVE: the same descriptors with source and destination swapped — packed
 // rows (hidden_out side) go back to their own rows of the full buffer
 // (hidden side); positions are not touched.
 template <int VW, bool REVIVE>
 __global__ void __launch_bounds__(kCopyThreads) up_compact_copy_kernel(CompactArgs a) {
+  if (!REVIVE && a.ledger && blockIdx.x == 0)
+    for (int r = threadIdx.x; r < a.num_seqs; r += kCopyThreads)
+      history_append_one(a.ledger, a.num_seqs, a.led_capacity, a.layer_id, a.cu_out, r);
   const int64_t items = a.num_blocks * a.pieces;
   for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
     int64_t b, piece;
@@ -584,7 +618,6 @@ __global__ void __launch_bounds__(kRowThreads) up_rowop_kernel(RowOpArgs a) {
 // ---------------------------------------------------------------------------
 // Drop-history ledger.
 // ---------------------------------------------------------------------------
-constexpr int kLedgerHeader = 4;
 
 __global__ void up_history_init_kernel(int32_t* led, int num_seqs, int capacity) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -600,21 +633,7 @@ __global__ void up_history_init_kernel(int32_t* led, int num_seqs, int capacity)
 __global__ void up_history_append_kernel(int32_t* led, int num_seqs, int capacity, int layer,
                                          const int32_t* cu_out) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= num_seqs) return;
-  if (led[1] != num_seqs || led[2] != capacity) {  // ledger set up for another shape
-    if (r == 0) atomicOr(&led[0], 2);
-    return;
-  }
-  const int cnt = led[kLedgerHeader + r];
-  const int kept = cu_out[r + 1] - cu_out[r];
-  if (cnt < capacity) {
-    int32_t* e = led + kLedgerHeader + num_seqs + 2 * ((int64_t)r * capacity + cnt);
-    e[0] = layer;
-    e[1] = kept;
-    led[kLedgerHeader + r] = cnt + 1;
-  } else {
-    atomicOr(&led[0], 1);
-  }
+  if (r < num_seqs) history_append_one(led, num_seqs, capacity, layer, cu_out, r);
 }
 
 // KV length per request for one layer: the kept count of the latest entry
@@ -700,6 +719,8 @@ struct GatherCall {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  int32_t* ledger = nullptr;  // up_compact_record: the ledger to append to
+  int led_capacity = 0, layer_id = 0;
 };
 
 template <bool REVIVE>
@@ -769,7 +790,18 @@ up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
   up::CompactArgs a;
   bool ran;
   up_status st = scan_for(c, T, &a, &ran);
-  if (st != UP_OK || !ran || a.num_blocks == 0) return st;
+  if (st != UP_OK || !ran) return st;
+  if (a.num_blocks == 0) {
+    if (!c.ledger) return st;
+    // nothing to copy: the ledger entries (all zero) by their own kernel
+    hipLaunchKernelGGL(up::up_history_append_kernel, dim3((unsigned)up::ceil_div(c.num_seqs, 256)),
+                       dim3(256), 0, c.stream, c.ledger, c.num_seqs, c.led_capacity, c.layer_id,
+                       c.cu_out);
+    return up::check_launch("up_history_append_kernel");
+  }
+  a.ledger = c.ledger;
+  a.led_capacity = c.led_capacity;
+  a.layer_id = c.layer_id;
   if (c.row_stride == c.row_bytes) {
     // kPieceBytes pieces, larger (4 KiB multiples) if a block would need more
     // than 65535 of them (keeps the item count of huge rows bounded)
@@ -963,6 +995,37 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
                block_mask, hidden,      row_bytes,        row_stride_bytes,
                positions, hidden_out,  positions_out,    cu_seqlens_out, out_capacity_rows,
                workspace, workspace_bytes, stream};
+  return run_gather(c, T, false);
+}
+
+up_status up_compact_record(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
+                            const int32_t* cu_blocks_d, int block, const uint8_t* block_mask,
+                            const void* hidden, int64_t row_bytes, int64_t row_stride_bytes,
+                            const int32_t* positions, void* hidden_out, int32_t* positions_out,
+                            int32_t* cu_seqlens_out, int64_t out_capacity_rows, void* workspace,
+                            size_t workspace_bytes, void* ledger, int capacity, int layer_id,
+                            hipStream_t stream) {
+  up::clear_error();
+  if (!ledger) return up::set_error(UP_ERR_INVALID, "ledger is NULL");
+  if (capacity < 1) return up::set_error(UP_ERR_INVALID, "need capacity >= 1");
+  int64_t T;
+  int max_len;
+  up_status st = up::check_cu_seqlens(num_seqs, cu_seqlens_h, &T, &max_len);
+  if (st != UP_OK) return st;
+  if (out_capacity_rows < T)
+    return up::set_error(UP_ERR_CAPACITY, "out_capacity_rows %lld < T %lld",
+                         (long long)out_capacity_rows, (long long)T);
+  if (!cu_seqlens_out || (T > 0 && (!hidden || !hidden_out)))
+    return up::set_error(UP_ERR_INVALID, "a required pointer is NULL");
+  if ((positions == nullptr) != (positions_out == nullptr))
+    return up::set_error(UP_ERR_INVALID, "positions and positions_out must both be set or both NULL");
+  GatherCall c{num_seqs,  cu_seqlens_h, cu_seqlens_d,     cu_blocks_d, block,
+               block_mask, hidden,      row_bytes,        row_stride_bytes,
+               positions, hidden_out,  positions_out,    cu_seqlens_out, out_capacity_rows,
+               workspace, workspace_bytes, stream};
+  c.ledger = static_cast<int32_t*>(ledger);
+  c.led_capacity = capacity;
+  c.layer_id = layer_id;
   return run_gather(c, T, false);
 }
 
