@@ -11,7 +11,8 @@ propagation can be checked and measured without a trained model:
 
   F  full-attention layer: Q and K projections of the RMS-normalised state
      (computed in both modes, as the layer's attention needs them) feed
-     up_score -> up_select_topp -> up_compact -> up_drop_history; the layer's
+     up_score -> up_select_topp -> up_compact_record (the compaction and the
+     drop-history append, up_compact + up_drop_history in one call); the layer's
      output projection then runs on the kept tokens only.
   L  token-local layer standing in for the layers between full-attention
      layers: a random two-matrix MLP with a residual, whose cost is
@@ -25,7 +26,7 @@ projections and MLPs are plain torch matrix products (contiguous operands).
 fused=True runs the fused pipeline at each F layer: no compacted copy of the
 hidden states is made; the layer's normalised operand is read straight from
 the frozen rows (up_compact_rmsnorm) and its residual sum reads the residual
-from them too (up_gather_add).  fused=False compacts first (up_compact) and
+from them too (up_gather_add).  fused=False compacts first (up_compact_record) and
 normalises / adds with torch.
 """
 from __future__ import annotations
@@ -35,7 +36,7 @@ from typing import List, Optional
 
 import torch
 
-from . import (Batch, up_compact, up_compact_rmsnorm, up_drop_history, up_gather_add,
+from . import (Batch, up_compact_record, up_compact_rmsnorm, up_drop_history, up_gather_add,
                up_history_bytes, up_history_init, up_score, up_score_workspace_size,
                up_select_topp, new_compact_workspace)
 
@@ -234,9 +235,8 @@ class HybridStack:
         h_out = torch.empty_like(h)
         p_out = torch.empty_like(pos)
         cu_out = torch.empty(B + 1, dtype=torch.int32, device=dev)
-        up_compact(cu, batch.cu_seqlens_d, batch.cu_blocks_d, cfg.block, mask, h, pos, h_out, p_out,
-                   cu_out, cws)
-        up_drop_history(ledger, B, nf, li, cu_out)
+        up_compact_record(cu, batch.cu_seqlens_d, batch.cu_blocks_d, cfg.block, mask, h, pos, h_out,
+                          p_out, cu_out, cws, ledger, nf, li)
         cu_new = cu_out.cpu()  # the next layer's packing sizes its launches on the host
         n = int(cu_new[-1])
         rec = None
