@@ -205,14 +205,23 @@ def main():
         run("up_select_topp", lambda: U.up_select_topp(
             batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, ws.block_scores, w.block,
             w.top_p, w.sink, w.tail, ws.block_mask, ws.kept_tokens))
+        copy_ev = marks.get("copy_kernel") if marks else None
+        if copy_ev:   # the library records these right around its copy kernel
+            U.up_set_copy_events(*copy_ev)
         run("up_compact_record", lambda: U.up_compact_record(
             batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, w.block, ws.block_mask,
             hidden, pos, ws.hidden_out, ws.positions_out, ws.cu_seqlens_out, ws.compact_ws,
             ledger, cap, layer % cap))
+        if copy_ev:
+            U.up_set_copy_events(None, None)
 
     def new_marks(names):
-        return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for n in names}
+        m = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for n in names}
+        if "copy_kernel" in m:   # handed to the library: create the HIP events now
+            for e in m["copy_kernel"]:
+                e.record()
+        return m
 
     def mean_us(marks_list, name):
         return float(np.mean([m[name][0].elapsed_time(m[name][1]) for m in marks_list])) * 1e3
@@ -239,13 +248,14 @@ def main():
     torch.cuda.synchronize()
     kept = int(ws.cu_seqlens_out[-1].item())
 
-    # Timed region: K steps; on every EVENT_EVERY-th step the two large calls
-    # (up_score, up_compact_record) are bracketed by events, and the larger of them
-    # over the timed region is the dominant one.  Each event record leaves
-    # the GPU idle for ~5 us, so bracketing every step would add ~11 us per
-    # call bracketed.
+    # Timed region: K steps; on every EVENT_EVERY-th step the two large
+    # pieces are bracketed by events: the up_score call, and the compaction
+    # copy kernel alone (events the library records right around its launch,
+    # up_set_copy_events); the larger of them over the timed region is the
+    # dominant one.  Each event record leaves the GPU idle for ~5 us, so
+    # bracketing every step would add ~11 us per piece bracketed.
     K = args.steps
-    big = ("up_score", "up_compact_record")
+    big = ("up_score", "copy_kernel")
     sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
     timed_marks = {i: new_marks(list(big)) for i in sampled}
     U.up_history_init(ledger, B, cap)
@@ -367,7 +377,8 @@ def main():
 
     ms_per_step = (t1 - t0) * 1e3 / K
     per_call_us = {n: med_us(brk, n) for n in calls}
-    per_call_us[dominant] = dominant_us
+    if dominant == "up_score":
+        per_call_us["up_score"] = dominant_us
     tokens_per_s = T / (ms_per_step / 1e3)
 
     # --- algorithmic work -------------------------------------------------
@@ -386,23 +397,21 @@ def main():
     t_score = per_call_us["up_score"] * 1e-6
     t_compact = per_call_us["up_compact_record"] * 1e-6
     t_select = per_call_us["up_select_topp"] * 1e-6
-    compact_gbs = compact_bytes / t_compact / 1e9
+    copy_us = mean_us(timed_marks, "copy_kernel")
+    copy_gbs = compact_bytes / (copy_us * 1e-6) / 1e9
     score_tflops_exec = flops_exec / t_score / 1e12
     score_tflops_alg = flops_alg / t_score / 1e12
 
-    if dominant == "up_compact_record":
-        # The copy kernel moves every byte; the events bracket the whole
-        # up_compact_record call (its small scan launch included), so
-        # `achieved` slightly understates the copy kernel's own rate.
-        tc = load_traffic("up_compact_copy_kernel", "up_compact.hip", w.name)
-        ts = load_traffic("up_compact_scan_kernel", "up_compact.hip", w.name)
-        traffic = tc + ts if tc is not None and ts is not None else None
-        roofline = {"kernel": "up_compact_copy_kernel", "bound": "hbm", "achieved": round(compact_gbs, 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
-                    "traffic": traffic,
+    if dominant == "copy_kernel":
+        # The copy kernel moves every byte the compaction moves; its events
+        # are recorded by the library right around its launch.
+        roofline = {"kernel": "up_compact_copy_kernel", "bound": "hbm", "achieved": round(copy_gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(copy_gbs / PEAK_HBM_GBS, 4),
+                    "traffic": load_traffic("up_compact_copy_kernel", "up_compact.hip", w.name),
                     "algorithmic_bytes_per_launch": int(compact_bytes),
-                    "duration": ("HIP events around up_compact_record (scan + copy launches) on every "
-                                 f"{EVENT_EVERY}th step of the timed region ({len(dom_all)} launches)")}
+                    "duration": ("HIP events recorded by the library right around the copy kernel's "
+                                 f"launch (up_set_copy_events) on every {EVENT_EVERY}th step of the "
+                                 f"timed region ({len(dom_all)} launches), mean {copy_us:.2f} us")}
     else:
         roofline = {"kernel": "up_score (rowstats+colsum+blockmean)", "bound": "mfma",
                     "achieved": round(score_tflops_exec, 1), "peak": PEAK_BF16_TFLOPS,
@@ -452,7 +461,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "breakdown_us": {k2: round(v, 2) for k2, v in per_call_us.items()},
-        "dominant_call_us": {"call": dominant, "p10": round(float(np.percentile(dom_all, 10)), 2),
+        "dominant_call_us": {"call": {"copy_kernel": "up_compact_copy_kernel (in up_compact_record)"}.get(dominant, dominant),
+                             "p10": round(float(np.percentile(dom_all, 10)), 2),
                              "median": round(float(np.median(dom_all)), 2),
                              "p90": round(float(np.percentile(dom_all, 90)), 2)},
         "chain_us_cold_cache": {"p10": round(float(np.percentile(cold_us, 10)), 2),

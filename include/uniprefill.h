@@ -301,6 +301,18 @@ up_status up_compact_noalloc(int num_seqs, const int32_t* cu_seqlens_h,
 up_status up_compact_status(void* workspace, size_t workspace_bytes, int32_t* status, int clear,
                             hipStream_t stream);
 
+/*
+ * up_set_copy_events — measurement aid.  While set, every call that runs the
+ * compaction copy kernel (up_compact, up_compact_record, up_compact_noalloc,
+ * up_revive) records `start` on its stream immediately before enqueuing that
+ * kernel and `stop` immediately after it, so hipEventElapsedTime(start, stop)
+ * times the copy kernel alone (the scan before it excluded).  Per host
+ * thread; NULL, NULL clears it (both or neither must be NULL, else
+ * UP_ERR_INVALID).  The events are the caller's (created on the device the
+ * calls run on, kept valid while set); a failed record returns UP_ERR_HIP.
+ */
+up_status up_set_copy_events(hipEvent_t start, hipEvent_t stop);
+
 /* ------------------------------------------------------------------------ */
 /* Step 5 (cont.): drop-history ledger (§三)                                  */
 /* ------------------------------------------------------------------------ */

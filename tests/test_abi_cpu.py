@@ -139,6 +139,13 @@ def test_compact_record_rejects_bad_arguments():
         assert st == status and msg in U.up_last_error(), (i, v, st, U.up_last_error())
 
 
+def test_copy_events_need_both_or_neither():
+    lib = U.lib()
+    assert lib.up_set_copy_events(16, None) == 1 and "both" in U.up_last_error()
+    assert lib.up_set_copy_events(None, 16) == 1
+    assert lib.up_set_copy_events(None, None) == 0   # clearing touches no device
+
+
 def test_history_rejects_bad_arguments():
     lib = U.lib()
     assert lib.up_history_init(None, 2, 4, None) == 1

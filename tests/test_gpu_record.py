@@ -136,3 +136,40 @@ def test_record_batch_without_blocks():
     ref = O.history_new(B)
     O.history_append(ref, 3, [0, 0, 0, 0])
     _check_ledger(led, ref, B, cap, 0)
+
+
+def test_copy_events_time_the_copy_kernel_alone():
+    """up_set_copy_events: the events land right around the copy kernel, so
+    their interval lies inside the whole call's and is positive; once
+    cleared, calls record nothing more into them."""
+    dev = torch.device("cuda")
+    lens = [70000, 0, 9000]
+    G = 64
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    batch = U.Batch.make(cu, G, dev)
+    T = batch.num_tokens
+    hidden = torch.ones((T, 2048), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(hidden)
+    cu_out = torch.empty(len(lens) + 1, dtype=torch.int32, device=dev)
+    mask = torch.ones(batch.num_blocks, dtype=torch.uint8, device=dev)
+    ws = U.new_compact_workspace(batch.cu_seqlens_h, G, dev)
+    c0, c1, o0, o1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    c0.record(); c1.record()
+    U.up_set_copy_events(c0, c1)
+    try:
+        o0.record()
+        U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, hidden,
+                     None, out, None, cu_out, ws)
+        o1.record()
+    finally:
+        U.up_set_copy_events(None, None)
+    torch.cuda.synchronize()
+    copy_ms, call_ms = c0.elapsed_time(c1), o0.elapsed_time(o1)
+    assert 0 < copy_ms < call_ms, (copy_ms, call_ms)
+    assert torch.equal(out, hidden)
+    # cleared: a further call leaves the events where they were
+    U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, hidden,
+                 None, out, None, cu_out, ws)
+    torch.cuda.synchronize()
+    assert c0.elapsed_time(c1) == copy_ms
+

@@ -23,7 +23,7 @@ __all__ = [
     "up_abi_version", "up_last_error", "up_make_cu_blocks",
     "up_score_workspace_size", "up_score", "up_select_topp",
     "up_compact_workspace_size", "up_compact_workspace_init", "up_compact", "up_compact_status",
-    "up_compact_noalloc", "up_compact_record",
+    "up_compact_noalloc", "up_compact_record", "up_set_copy_events",
     "up_history_bytes", "up_history_init", "up_drop_history", "up_kv_len", "up_revive",
     "up_compact_rmsnorm", "up_gather_add", "up_score_select",
     "Batch", "Workspace", "run_chain",
@@ -72,6 +72,7 @@ _SIGNATURES = {
     "up_compact_record": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P,
                                _SZ, _P, _I, _I, _P]),
     "up_compact_status": (_I, [_P, _SZ, _P, _I, _P]),
+    "up_set_copy_events": (_I, [_P, _P]),
     "up_compact_noalloc": (_I, [_I, _P, _P, _P, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P,
                                 _P]),
     "up_history_bytes": (_SZ, [_I, _I]),
@@ -299,6 +300,20 @@ def up_compact_status(workspace, status, clear: bool = True, stream=None) -> Non
     _check("up_compact_status", lib().up_compact_status(_ptr(workspace), workspace.numel(),
                                                         _ptr(status), 1 if clear else 0,
                                                         _stream(stream, workspace.device)))
+
+
+def up_set_copy_events(start=None, stop=None) -> None:
+    """Measurement aid: while set, calls that run the compaction copy kernel
+    record the two torch.cuda.Event objects right around it (None, None
+    clears).  Record each event once beforehand: torch creates the
+    underlying HIP event on its first record."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:
+            raise ValueError("event not created yet: record it once first")
+        return ctypes.c_void_p(ev.cuda_event)
+    _check("up_set_copy_events", lib().up_set_copy_events(handle(start), handle(stop)))
 
 
 def up_history_init(ledger, num_seqs: int, capacity: int, stream=None) -> None:

@@ -723,6 +723,10 @@ struct GatherCall {
   int led_capacity = 0, layer_id = 0;
 };
 
+// Measurement hook (up_set_copy_events): events recorded on the call's stream
+// right before and right after the copy kernel is enqueued, per host thread.
+thread_local hipEvent_t t_copy_start = nullptr, t_copy_stop = nullptr;
+
 template <bool REVIVE>
 void launch_copy(const up::CompactArgs& a, dim3 grid, uintptr_t al, hipStream_t stream) {
   if ((al & 15) == 0)
@@ -821,9 +825,14 @@ up_status run_gather(const GatherCall& c, int64_t T, bool revive) {
   const dim3 grid((unsigned)(items < (int64_t)1 << 30 ? items : (int64_t)1 << 30));
   const uintptr_t al = (uintptr_t)c.hidden | (uintptr_t)c.hidden_out | (uintptr_t)c.row_bytes |
                        (uintptr_t)c.row_stride;
+  if (t_copy_start && hipEventRecord(t_copy_start, c.stream) != hipSuccess)
+    return up::set_error(UP_ERR_HIP, "hipEventRecord (copy start event) failed");
   if (revive) launch_copy<true>(a, grid, al, c.stream);
   else launch_copy<false>(a, grid, al, c.stream);
-  return up::check_launch("up_compact_copy_kernel");
+  st = up::check_launch("up_compact_copy_kernel");
+  if (st == UP_OK && t_copy_stop && hipEventRecord(t_copy_stop, c.stream) != hipSuccess)
+    return up::set_error(UP_ERR_HIP, "hipEventRecord (copy stop event) failed");
+  return st;
 }
 
 // ---------------------------------------------------------------------------
@@ -996,6 +1005,15 @@ up_status up_compact(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
                positions, hidden_out,  positions_out,    cu_seqlens_out, out_capacity_rows,
                workspace, workspace_bytes, stream};
   return run_gather(c, T, false);
+}
+
+up_status up_set_copy_events(hipEvent_t start, hipEvent_t stop) {
+  up::clear_error();
+  if ((start == nullptr) != (stop == nullptr))
+    return up::set_error(UP_ERR_INVALID, "start and stop events must both be set or both NULL");
+  t_copy_start = start;
+  t_copy_stop = stop;
+  return UP_OK;
 }
 
 up_status up_compact_record(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu_seqlens_d,
