@@ -226,9 +226,10 @@ up_status up_compact_workspace_init(void* workspace, size_t workspace_bytes, hip
  * workspace        >= up_compact_workspace_size bytes, 256-byte aligned,
  *                  prepared by up_compact_workspace_init (and then only
  *                  used by up_compact calls, one at a time).
- * Two kernel launches: a single-pass decoupled look-back scan (Merrill &
- * Garland 2016) over tiles of 1024 blocks writes each block's output row
- * and cu_seqlens_out (tiles are claimed in order from an atomic counter, so
+ * Two kernel launches: a scan that writes each block's output row and
+ * cu_seqlens_out — one workgroup for a batch of at most 4096 blocks, else a
+ * single-pass decoupled look-back scan (Merrill & Garland 2016) over tiles
+ * of 1024 blocks (tiles are claimed in order from an atomic counter, so
  * every predecessor a tile waits on has started; a wait that still exceeds
  * the poll limit gives up and sets status bit 0, read with
  * up_compact_status; the last tile to finish restores the workspace's

@@ -222,7 +222,7 @@ def test_compact_lookback_give_up_is_reported():
     word stays set until read and cleared; the workspace then serves a normal
     call again."""
     G = 16
-    L = 1100 * G                      # 1100 blocks: two scan tiles of 1024
+    L = 4200 * G   # 4200 blocks: five scan tiles of 1024 (above 4096, so the look-back scan runs)
     cu = torch.tensor([0, L], dtype=torch.int32)
     batch = U.Batch.make(cu, G, DEV)
     gen = torch.Generator().manual_seed(5)

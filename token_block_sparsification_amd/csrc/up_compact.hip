@@ -7,7 +7,9 @@
 // tokens) to the request's drop-history ledger.
 //
 // up_compact is two kernels.
-//   up_compact_scan_kernel   single-pass decoupled look-back scan (Merrill &
+//   up_compact_scan_kernel   a batch of at most 4096 blocks is one tile that
+//     one 1024-thread workgroup scans alone; larger ones run a single-pass
+//     decoupled look-back scan (Merrill &
 //     Garland, "Single-pass Parallel Prefix Scan with Decoupled Look-back",
 //     2016) over tiles of 1024 blocks: each workgroup claims the next tile
 //     from an atomic ticket (so every tile it may wait on has already
@@ -43,6 +45,10 @@ namespace {
 constexpr int kCompactThreads = 256;
 constexpr int kScanPerThread = 4;
 constexpr int kScanTileBlocks = kCompactThreads * kScanPerThread;  // blocks per scan tile
+// Batches of at most kScan1Blocks blocks are scanned by one workgroup of
+// kScan1Threads threads (one tile, nothing to look back on).
+constexpr int kScan1Threads = 1024;
+constexpr int kScan1Blocks = kScan1Threads * kScanPerThread;
 // Copy work items: 4 KiB per 128-thread workgroup, one 16-byte vector in
 // flight per lane (two rounds).  Many short-lived workgroups keep more HBM
 // requests in flight across the chip than fewer long ones.  Per up_compact
@@ -141,16 +147,25 @@ __device__ __forceinline__ int block_request(const int32_t* cu_blocks, int num_s
   return lo;
 }
 
-__global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(CompactArgs a) {
+// NTH threads, kScanPerThread blocks each, per tile.  ONE: the whole batch
+// is one tile of one workgroup (at most kScan1Blocks blocks), so there is no
+// ticket, no look-back and no done counter; that form leaves the control
+// words and the tile status words untouched (it writes descriptors and
+// cu_seqlens_out only), which keeps the workspace as prepared.
+template <int NTH, bool ONE>
+__global__ void __launch_bounds__(NTH) up_compact_scan_kernel(CompactArgs a) {
+  constexpr int kTileBlocks = NTH * kScanPerThread;
   __shared__ int64_t s_tile;
   __shared__ int64_t s_excl;
-  __shared__ int64_t s_wave[kCompactThreads / 64];
+  __shared__ int64_t s_wave[NTH / 64];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) s_tile = (int64_t)atomicAdd(&a.ctl[0], 1u);
-  __syncthreads();
-  const int64_t t = s_tile;
+  if (!ONE) {
+    if (tid == 0) s_tile = (int64_t)atomicAdd(&a.ctl[0], 1u);
+    __syncthreads();
+  }
+  const int64_t t = ONE ? 0 : s_tile;
   const uint32_t poll_limit = a.ctl[3] ? a.ctl[3] : kSpinLimit;
   // This call's epoch: the last workgroup advances it only after every
   // workgroup of the call has counted itself done, so all read one value.
@@ -164,9 +179,9 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
     for (int r = 0; r < a.num_seqs && a.cu_blocks[r + 1] == 0; ++r) a.cu_out[r + 1] = 0;
   }
 
-  if (t < a.num_tiles) {
+  if (ONE || t < a.num_tiles) {
     // This thread's blocks: kScanPerThread consecutive ones.
-    const int64_t b0 = t * kScanTileBlocks + (int64_t)tid * kScanPerThread;
+    const int64_t b0 = t * kTileBlocks + (int64_t)tid * kScanPerThread;
     int req[kScanPerThread], rows[kScanPerThread];
     int64_t kept[kScanPerThread];
     int64_t mine = 0;
@@ -193,12 +208,14 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
     __syncthreads();
     int64_t wbase = 0, agg = 0;
 #pragma unroll
-    for (int w = 0; w < kCompactThreads / 64; ++w) {
+    for (int w = 0; w < NTH / 64; ++w) {
       if (w < wave) wbase += s_wave[w];
       agg += s_wave[w];
     }
 
-    if (wave == 0) {
+    if (ONE) {
+      if (tid == 0) s_excl = 0;
+    } else if (wave == 0) {
       // Publish this tile's count, then look back a window of 64
       // predecessors per round trip: lane i reads tile (hi - i); the nearest
       // tile that already has an inclusive prefix ends the walk.
@@ -263,6 +280,7 @@ __global__ void __launch_bounds__(kCompactThreads) up_compact_scan_kernel(Compac
     }
   }
 
+  if (ONE) return;
   // Done counter: the last workgroup leaves the tile status words and the
   // two counters zeroed and advances the epoch for the next call (every
   // other workgroup has finished its look-back before it counted itself
@@ -783,8 +801,12 @@ up_status scan_for(const GatherCall& c, int64_t T, up::CompactArgs* out, bool* r
   a.block = c.block;
   a.num_blocks = lay.blocks;
   a.num_tiles = lay.tiles;
-  hipLaunchKernelGGL(up::up_compact_scan_kernel, dim3((unsigned)(a.num_tiles > 0 ? a.num_tiles : 1)),
-                     dim3(up::kCompactThreads), 0, c.stream, a);
+  if (a.num_blocks <= up::kScan1Blocks)
+    hipLaunchKernelGGL((up::up_compact_scan_kernel<up::kScan1Threads, true>), dim3(1),
+                       dim3(up::kScan1Threads), 0, c.stream, a);
+  else
+    hipLaunchKernelGGL((up::up_compact_scan_kernel<up::kCompactThreads, false>),
+                       dim3((unsigned)a.num_tiles), dim3(up::kCompactThreads), 0, c.stream, a);
   st = up::check_launch("up_compact_scan_kernel");
   *ran = st == UP_OK;
   return st;
