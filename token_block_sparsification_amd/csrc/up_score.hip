@@ -476,20 +476,61 @@ __device__ __forceinline__ void rowstats_update(f32x16_t acc, int t, bool masked
   m_run[t] = mx;
 }
 
+// Three-stage form of pass A's pipeline: the VALU works on group q while the
+// MFMAs of groups q+1 (issued one group earlier) and q+2 run, so no group's
+// VALU work waits for the MFMA chain issued just before it (kernel traces at
+// 128K: 146.4-146.5 vs 150.0-150.5 us; 32K: 45.8-46.2 vs 46.5-46.8 us).  Only
+// the 8-wave tilings take it: with 4 waves per workgroup each wave keeps
+// twice the K-fetch addresses, and the third accumulator spills (256 VGPRs).
+#ifndef UP_PIPE3_A
+#define UP_PIPE3_A 1
+#endif
+template <int D, int NT, int W, bool PIPE>
+constexpr bool pipe3_a() {
+  return UP_PIPE3_A && PIPE && NT == 2 && W == 8 && KTile<D, W>::KT / 32 >= 2;
+}
+
 // One LDS tile: NG = (KT/32)*NT groups, ordered (mt, t).  On entry acc holds
 // the (issued) S of group 0 of this tile and af the A fragments of mt = 0;
 // on exit they hold group 0 of the next tile (from `nxt`).  The pipelined
 // form with NT >= 2 reads each sub-tile's fragments while the previous
-// sub-tile's last group issues, so no MFMA waits on its LDS read.
+// sub-tile's last group issues, so no MFMA waits on its LDS read.  In the
+// three-stage form (pipe3_a) acc and acc1 hold groups 0 and 1 and af the
+// fragments of sub-tile 1 on entry, and the same of the next tile on exit.
 template <int D, int NT, int W, bool MASKED, bool PIPE>
 __device__ __forceinline__ void rowstats_iter(const uint16_t* cur, const uint16_t* nxt, int tkey0,
                                               int key1, int lane, float C,
                                               const bf16x8_t (&qf)[NT][D / 16],
                                               const int (&ipos)[NT], float (&m_run)[NT],
-                                              float (&l_run)[NT], f32x16_t& acc,
+                                              float (&l_run)[NT], f32x16_t& acc, f32x16_t& acc1,
                                               bf16x8_t (&af)[D / 16]) {
   constexpr int KT = KTile<D, W>::KT;
   constexpr int NG = (KT / 32) * NT;
+  if constexpr (!MASKED && pipe3_a<D, NT, W, PIPE>()) {
+    constexpr int SPT = KT / 32;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const int mt = q / NT, t = q % NT;
+      const int mt2 = (q + 2) / NT, t2 = (q + 2) % NT;  // group q+2; mt2 >= SPT: next tile
+      // af holds sub-tile mt2; its last group replaces each fragment by the
+      // next sub-tile's right after the MFMA that reads it
+      const bool roll = t2 == NT - 1;
+      const int ns = mt2 + 1;
+      const uint16_t* src = ns < SPT ? cur : nxt;
+      const int nsub = ns < SPT ? ns : ns - SPT;
+      f32x16_t nacc = {};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        nacc = mfma32(af[s], qf[t2][s], nacc);
+        if (roll) af[s] = load_frag<D, W>(src, nsub, lane, s);
+      }
+      rowstats_update<NT>(acc, t, false, tkey0 + mt * 32, key1, lane, C, ipos, m_run, l_run);
+      acc = acc1;
+      acc1 = nacc;
+      if (roll) interleave_hint_roll<D>(); else interleave_hint<D>();
+    }
+    return;
+  }
   if constexpr (!PIPE) {
 #pragma unroll
     for (int mt = 0; mt < KT / 32; ++mt) {
@@ -613,11 +654,16 @@ up_rowstats_kernel(ScoreArgs a) {
   const int nfull = (key1 - key0) / KT;
   const int nmain = max(0, min(nfast, nfull - (RING - 1)));
   if (nfast > 0) {
-    f32x16_t acc = {};
+    f32x16_t acc = {}, acc1 = {};
     if constexpr (PIPE) {
       load_frags<D, W>(kl[0], 0, lane, af);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) acc = mfma32(af[s], qf[0][s], acc);
+      if constexpr (pipe3_a<D, NT, W, PIPE>()) {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) acc1 = mfma32(af[s], qf[1][s], acc1);
+        load_frags<D, W>(kl[0], 1, lane, af);
+      }
     }
     // Steady state unrolled over kUnroll tiles; with a ring of kUnroll slots
     // every LDS slot address is a compile-time constant (it starts at 0).
@@ -627,7 +673,7 @@ up_rowstats_kernel(ScoreArgs a) {
       ks.fetch_full(it + U + RING - 1, kl[(s0 + U + RING - 1) % RING]);
       rowstats_iter<D, NT, W, false, PIPE>(kl[(s0 + U) % RING], kl[(s0 + U + 1) % RING],
                                            key0 + (it + U) * KT, key1, lane, C, qf, ipos, m_run,
-                                           l_run, acc, af);
+                                           l_run, acc, acc1, af);
       ring_step<RING, Tile, true>();
     };
     for (; it + kUnroll <= nmain; it += kUnroll) static_for<0, kUnroll>(step);
@@ -635,15 +681,15 @@ up_rowstats_kernel(ScoreArgs a) {
       const bool more = it + RING - 1 < ntiles;
       if (more) ks.fetch(it + RING - 1, kl[(it + RING - 1) % RING]);
       rowstats_iter<D, NT, W, false, PIPE>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT,
-                                           key1, lane, C, qf, ipos, m_run, l_run, acc, af);
+                                           key1, lane, C, qf, ipos, m_run, l_run, acc, acc1, af);
       if (more) ring_step<RING, Tile, true>(); else ring_step<RING, Tile, false>();
     }
   }
   for (; it < ntiles; ++it) {
     if (it + RING - 1 < ntiles) ks.fetch(it + RING - 1, kl[(it + RING - 1) % RING]);
-    f32x16_t acc = {};
+    f32x16_t acc = {}, acc1 = {};
     rowstats_iter<D, NT, W, true, false>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT, key1,
-                                         lane, C, qf, ipos, m_run, l_run, acc, af);
+                                         lane, C, qf, ipos, m_run, l_run, acc, acc1, af);
     ring_step<RING, Tile, false>();
   }
 
