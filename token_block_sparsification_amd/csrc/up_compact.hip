@@ -374,8 +374,9 @@ __device__ __forceinline__ void history_append_one(int32_t* led, int num_seqs, i
 
 // Work item w = (block w / pieces, piece w % pieces): consecutive workgroups
 // copy consecutive pieces of one block, so the streams stay sequential in
-// memory.  With a ledger, workgroup 0 first appends every request's entry
-// from cu_seqlens_out (written by the scan, the launch before).  A grid-stride loop covers batches with more items than one grid.
+// memory.  A grid-stride loop covers batches with more items than one grid.
+// With a ledger, workgroup 0 first appends every request's entry from
+// cu_seqlens_out (written by the scan, the launch before).
 // REVIVE: the same descriptors with source and destination swapped — packed
 // rows (hidden_out side) go back to their own rows of the full buffer
 // (hidden side); positions are not touched.
