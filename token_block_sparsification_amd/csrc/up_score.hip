@@ -1238,6 +1238,10 @@ __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
 #ifndef UP_TILE_A64_ONE_ROUND
 #define UP_TILE_A64_ONE_ROUND UP_TILE_A64
 #endif
+// Pass B at head_dim 256: one 8-wave workgroup of 32-row tiles per CU, also
+// over several rounds (Qwen3-Next shape, per call: n = 32 97-98 vs 99-100 us,
+// n = 128 288-296 vs 302-311 us, n = 512 1026-1028 vs 1063-1065 us against
+// two 4-wave workgroups).
 #ifndef UP_TILE_B256
 #define UP_TILE_B256 1, 8, true, 4
 #endif
