@@ -14,8 +14,11 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_chain_graph_replays_match_eager(fused):
+@pytest.mark.parametrize("mode", ["plain", "fused", "record"])
+def test_chain_graph_replays_match_eager(mode):
+    """plain: the four calls; fused: the fused pipeline; record: the
+    benchmark's step (up_score, up_select_topp, up_compact_record)."""
+    fused = mode == "fused"
     dev = torch.device("cuda")
     w = W.get_workload("small_L2048").with_(lengths=(2048, 700, 0, 96, 1500), num_seqs=5,
                                             hidden_dim=256, hidden_dtype="bf16")
@@ -39,6 +42,15 @@ def test_chain_graph_replays_match_eager(fused):
                                  ws.block_mask, hidden, None, 1e-6, pos, normed, ws.hidden_out,
                                  ws.positions_out, ws.cu_seqlens_out, ws.compact_ws)
             U.up_drop_history(ledger, B, cap, 3, ws.cu_seqlens_out)
+        elif mode == "record":
+            U.up_score(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, q, k, w.n_query,
+                       w.block, 0.0, ws.token_scores, ws.block_scores, ws.score_ws)
+            U.up_select_topp(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d,
+                             ws.block_scores, w.block, w.top_p, w.sink, w.tail, ws.block_mask,
+                             ws.kept_tokens)
+            U.up_compact_record(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, w.block,
+                                ws.block_mask, hidden, pos, ws.hidden_out, ws.positions_out,
+                                ws.cu_seqlens_out, ws.compact_ws, ledger, cap, 3)
         else:
             U.run_chain(batch, ws, q, k, hidden, pos, ledger, cap, layer_id=3, n_query=w.n_query,
                         top_p=w.top_p, sink=w.sink, tail=w.tail)

@@ -156,7 +156,8 @@ def _intact(whole, nbytes, fill=0xA5):
 def test_guard_bands_around_every_output():
     """Sentinel bytes before and after every buffer the path writes (scores,
     mask, kept counts, compacted rows and positions, cu_seqlens_out, both
-    workspaces, the ledger, revival target, KV lengths) are untouched."""
+    workspaces, the ledger — also through up_compact_record, which fills its
+    last record — revival target, KV lengths) are untouched."""
     w = W.get_workload("small_L2048").with_(lengths=(700, 2048, 96, 1500, 1), num_seqs=5)
     inp = W.make_inputs(w)
     G, n_q = w.block, w.n_query
@@ -203,6 +204,8 @@ def test_guard_bands_around_every_output():
         U.up_drop_history(ledger, B, 3, layer, cu_out)
     U.up_score_select(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, q, k, n_q, G,
                       0.0, ts, bs, 0.9, 64, 192, mask, kept, score_ws)
+    U.up_compact_record(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, hidden,
+                        pos, h_out, p_out, cu_out, compact_ws, ledger, 3, 8)
     U.up_revive(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, h_out, full,
                 compact_ws)
     U.up_kv_len(ledger, B, 3, 4, batch.cu_seqlens_d, kv)
