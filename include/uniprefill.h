@@ -17,7 +17,7 @@
  *   up_kv_len       per-layer KV length read back from the ledger
  *   up_revive       scatter of packed kept rows back into the full buffer
  * and, fused:
- *   up_score_select     up_score + up_select_topp, selecting in the column-sum kernel
+ *   up_score_select     up_score + up_select_topp, selecting in the block-mean kernel
  *   up_compact_record   up_compact + up_drop_history, appending in the copy kernel
  * and, fused into the next layer's first reads (no compacted copy),
  *   up_compact_rmsnorm  normalised input operand of the kept rows
@@ -384,15 +384,15 @@ up_status up_revive(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* cu
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
-/* Fused pipeline: selection inside the column-sum kernel (§三)              */
+/* Fused pipeline: selection inside the block-mean kernel (§三)             */
 /* ------------------------------------------------------------------------ */
 
 /*
- * up_score_select — up_score followed by up_select_topp in one call of two
- * launches (§三: scores, block aggregation and the binary mask without a
- * round trip).  The last of a key chunk's column-sum workgroups to finish
- * computes the chunk's token and block scores, and the workgroup that
- * finishes a request's last chunk selects that request's blocks.
+ * up_score_select — up_score followed by up_select_topp in one call of
+ * three launches (§三: scores, block aggregation and the binary mask without
+ * a round trip): the two scoring passes, then one kernel that computes the
+ * token and block scores and, in the workgroup that writes a request's last
+ * block mean, selects that request's blocks.
  * Outputs are bit-identical to up_score then up_select_topp with the same
  * arguments (same sums in the same order; the same selection code on the
  * same block scores).  Arguments: those of up_score, then those of

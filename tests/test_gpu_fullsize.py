@@ -72,7 +72,7 @@ def test_qwen3next_sweep(n, G):
 
 def test_fused_pipeline_full_size():
     """The fused pipeline at the benchmark's full size (one 131072-token
-    request, hidden 4096 bf16): the selection run by the column-sum kernel
+    request, hidden 4096 bf16): the selection run by the block-mean kernel
     gives bit-identical scores, mask and kept counts to the two calls; the normalised operand
     and the residual sum are checked against the oracle on 1024 sampled kept
     rows (operand within half a bf16 ulp plus the fp32 error bound, residual

@@ -157,16 +157,17 @@ SEL_CASES = [
     ("long_d256", dict(lengths=(20000, 3000), hq=16, hkv=2, head_dim=256, n_query=128, block=128)),
     # a request of 4375 blocks: more than the selection stages in LDS
     ("many_blocks_d64", dict(lengths=(70000, 100), hq=2, hkv=1, head_dim=64, n_query=16, block=16)),
-    # column-sum chunks rounded up from 320 keys to whole 256-token blocks
-    ("rounded_chunks_G256", dict(lengths=(9000, 7000, 5000, 12000, 3000), hq=8, hkv=2,
+    # column-sum chunks of 320 keys: 256-token blocks straddle chunks
+    ("straddling_chunks_G256", dict(lengths=(9000, 7000, 5000, 12000, 3000), hq=8, hkv=2,
                                  head_dim=128, n_query=128, block=256)),
 ]
 
 
 @pytest.mark.parametrize("name,kw", SEL_CASES, ids=[c[0] for c in SEL_CASES])
 def test_score_select_matches_two_calls(name, kw):
-    """Selection run by the column-sum kernel (the workgroup that completes a
-    request's last key chunk): scores, mask and kept counts are
+    """Selection run by the block-mean kernel (the workgroup that writes a
+    request's last block mean; one workgroup's blocks may span several
+    requests, some empty): scores, mask and kept counts are
     bit-identical to up_score followed by up_select_topp, and the mask and
     counts agree with the oracle's selection on the GPU's block scores.  The
     same workspace then serves a second, smaller batch (the arrival counters

@@ -104,8 +104,7 @@ def test_long_chunk_boundaries():
 
 
 def _column_sum_chunk(lengths, hkv, rg):
-    """The column-sum pass's key chunk before it is rounded to whole blocks
-    (the host rule: whole rounds of 512 workgroups, chunks of 256 + 64 i keys
+    """The column-sum pass's key chunk (the host rule: whole rounds of 512 workgroups, chunks of 256 + 64 i keys
     minimising rounds x (chunk + 256), longer on ties), given the row-statistics
     chunk 256 that these test batches get."""
     per_round = max(1, 512 // (hkv * rg))
@@ -119,15 +118,15 @@ def _column_sum_chunk(lengths, hkv, rg):
 
 
 @pytest.mark.parametrize("G", [128, 256])
-def test_chunks_rounded_to_whole_blocks(G):
+def test_blocks_straddling_column_sum_chunks(G):
     """The column-sum chunk that the rounds rule picks (320 keys here) holds no
-    whole number of 128- or 256-token blocks; the pass rounds it up so that
-    every chunk's last workgroup can average whole blocks.  Ragged requests,
+    whole number of 128- or 256-token blocks, so blocks straddle chunks and a
+    block mean adds token scores from two chunks' partials.  Ragged requests,
     a 3000-token one with a short last block."""
     lengths = (9000, 7000, 5000, 12000, 3000)
     ck = _column_sum_chunk(lengths, hkv=2, rg=2)
     assert ck == 320 and ck % G != 0
-    w = W.Workload(name=f"rounded_chunks_G{G}", lengths=lengths, hq=8, hkv=2, head_dim=128,
+    w = W.Workload(name=f"straddling_chunks_G{G}", lengths=lengths, hq=8, hkv=2, head_dim=128,
                    hidden_dim=64, hidden_dtype="bf16", seed=6150 + G, plant_frac=0.05,
                    num_seqs=len(lengths))
     _end_to_end(W.make_inputs(w), 128, G, name=w.name)

@@ -207,7 +207,7 @@ def up_score_select(cu_seqlens_h, cu_seqlens_d, cu_blocks_d, q, k, n_query: int,
                     top_p: float, sink: int, tail: int, block_mask, kept_tokens,
                     workspace: torch.Tensor, stream=None) -> None:
     """up_score and up_select_topp in one call, the selection run by the
-    column-sum kernel (fused pipeline); same outputs as the two calls."""
+    block-mean kernel (fused pipeline); same outputs as the two calls."""
     _bf16_3d("q", q)
     _bf16_3d("k", k)
     cu = _host_i32(cu_seqlens_h)

@@ -37,8 +37,7 @@ struct ScoreGeometry {
   int ck;            // keys per row-statistics workgroup chunk (sets the partials layout)
   int ck_b;          // keys per column-sum workgroup chunk
   int max_chunks;    // chunks of the longest request
-  int chunks_b;      // column-sum chunk counters per request (chunks of >= 256 keys)
-  size_t off_partial, off_colpart, off_arrive, off_chunk_arrive, bytes;
+  size_t off_partial, off_colpart, off_arrive, bytes;
 };
 
 ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int hkv,

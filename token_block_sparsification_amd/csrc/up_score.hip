@@ -20,10 +20,10 @@
 //   up_score: up_blockmean_kernel then sums the partials over (KV head, row
 //           group) in a fixed order (token score) and averages each block
 //           (block score).
-//   up_score_select: the column-sum kernel does that itself: the last of a
-//           key chunk's workgroups to finish sums and averages the chunk's
-//           keys, and the workgroup that finishes a request's last chunk
-//           runs its Top-p selection (no further launch).
+//   up_score_select: up_blockmean_select_kernel computes the same token and
+//           block scores and, in the workgroup that writes a request's last
+//           block mean, runs that request's Top-p selection (no further
+//           launch).
 // No floating-point atomics anywhere: results are bitwise reproducible.
 #include <math.h>
 
@@ -89,8 +89,6 @@ struct ScoreArgs {
   float* block_scores;
   int64_t num_blocks;
   uint32_t* arrive;        // [B] chunks of each request done (fused selection)
-  uint32_t* chunk_arrive;  // [B][chunks_b] column-sum workgroups of each chunk done
-  int chunks_b;            // per-request stride of chunk_arrive
   int32_t* kept;           // fused selection: kept tokens [B] (requests without blocks get 0 here)
 };
 
@@ -101,15 +99,13 @@ __global__ void up_zero_kernel(int32_t* p, int n) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Relaxed device-scope atomic store / load: coherent across the XCDs' L2
-// caches without an L2 write-back or invalidate (the stores write through
-// to memory).  Values one workgroup hands to another inside a kernel go
-// through these, ordered by the arrival counters (arrive_last).
+// Relaxed device-scope atomic store: coherent across the XCDs' L2 caches
+// without an L2 write-back or invalidate (it writes through to memory).
+// Values one workgroup hands to another inside a kernel go through it,
+// ordered by the arrival counters (arrive_last), and are read with the
+// selection's coherent loads.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
@@ -592,11 +588,9 @@ up_rowstats_kernel(ScoreArgs a) {
   constexpr int KT = Tile::KT;
   __shared__ __attribute__((aligned(16))) uint16_t kl[RING][Tile::ELEMS];
 
-  // The arrival counters of this call's column-sum pass start at zero (that
-  // pass runs after this one, and this one after the previous call).
+  // The arrival counters of this call's block-mean/selection kernel start
+  // at zero (it runs after this one, and this one after the previous call).
   if (blockIdx.x == 0) {
-    const int64_t ncnt = (int64_t)a.num_seqs * a.chunks_b;
-    for (int64_t i = threadIdx.x; i < ncnt; i += 64 * W) a.chunk_arrive[i] = 0;
     for (int r = threadIdx.x; r < a.num_seqs; r += 64 * W) {
       a.arrive[r] = 0;
       // a request without blocks never reaches the selection
@@ -868,7 +862,7 @@ __device__ __forceinline__ void colsum_iter_db(const uint16_t* cur, const uint16
 // order, for its KT/W keys and writes them.  All 64 lanes run it; lanes that
 // share a key store the same value, so no lane mask splits the caller's
 // block.  FULL: every key of the tile is below key1.
-template <int W, int KT, bool FULL, bool COH>
+template <int W, int KT, bool FULL>
 __device__ __forceinline__ void colsum_flush(const float (*colrow)[64], int wave, int lane, int tkey0,
                                              int key1, float* colout) {
   constexpr int KPW = KT / W;
@@ -877,108 +871,18 @@ __device__ __forceinline__ void colsum_flush(const float (*colrow)[64], int wave
   float sum = 0.f;
 #pragma unroll
   for (int w = 0; w < W; ++w) sum += colrow[w][k];
-  if (FULL || tkey0 + k < key1) {
-    if constexpr (COH) store_coherent(&colout[tkey0 + k], sum);
-    else colout[tkey0 + k] = sum;
-  }
+  if (FULL || tkey0 + k < key1) colout[tkey0 + k] = sum;
 }
 
-// ---------------------------------------------------------------------------
-// Chunk epilogue of the column-sum pass.
-// ---------------------------------------------------------------------------
-
-// Count this workgroup in *counter once its coherent stores (store_coherent)
-// have completed; true, in every thread, in the workgroup that brings the
-// count to `expect`.  Every wave waits until its stores are acknowledged
-// (written through to memory) before the one thread counts, so the
-// workgroup that reads the final count finds every counted workgroup's
-// coherent stores with load_coherent.  No L2 write-back or invalidate.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expect, uint32_t& flag) {
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    flag = prev + 1 == expect ? 1u : 0u;
-  }
-  __syncthreads();
-  return flag != 0;
-}
-
-// Token scores of keys [key0, key1) of request req: the column partials
-// summed over (KV head, row group) in that order, written to token_scores
-// (when given) and to `cs` (LDS); then each block's score, the mean of its
-// tokens: one wave per block sums them lane-strided, then across the wave.
-// Chunks hold whole blocks (their first key is a multiple of the block
-// size).  Every thread of the NTH-thread workgroup calls it.
-template <int NTH>
-__device__ void chunk_scores(const ScoreArgs& a, int req, int s0, int key0, int key1, int rg_used,
-                             float* cs) {
-  constexpr int KPT = (UP_CK_MAX + NTH - 1) / NTH;  // keys per thread
-  constexpr int PB = 4;  // partials loaded per batch, all in flight together
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nk = key1 - key0;
-  const int np = a.hkv * rg_used;
-  const float* part = a.colpart + s0 + key0 + tid;
-  float c[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) c[u] = 0.f;
-  for (int p0 = 0; p0 < np; p0 += PB) {
-    float v[PB][KPT];
-#pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int p = min(p0 + i, np - 1);
-      const int g = p / rg_used, rgi = p - g * rg_used;
-      const float* pp = part + ((int64_t)g * a.rg + rgi) * a.T;
-#pragma unroll
-      for (int u = 0; u < KPT; ++u)
-        v[i][u] = (p0 + i < np && tid + u * NTH < nk) ? load_coherent(pp + u * NTH) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < PB; ++i)
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) c[u] += v[i][u];  // + 0 past the last partial: exact
-  }
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int j = tid + u * NTH;
-    if (j < nk) {
-      cs[j] = c[u];
-      if (a.token_scores) a.token_scores[s0 + key0 + j] = c[u];
-    }
-  }
-  __syncthreads();
-  const int G = a.block;
-  const int nbk = (nk + G - 1) / G;
-  const int64_t b0 = a.cu_blocks[req] + key0 / G;
-  for (int i = wave; i < nbk; i += NTH / 64) {
-    const int j0 = i * G, j1 = min(j0 + G, nk);
-    float sum = 0.f;
-    for (int j = j0 + lane; j < j1; j += 64) sum += cs[j];
-    sum = wave_sum_f32(sum);
-    if (lane == 0) store_coherent(&a.block_scores[b0 + i], sum / (float)(j1 - j0));
-  }
-}
-
-// Largest number of blocks the selection may stage in LDS when its state
-// must fit `BYTES` (the column-sum kernel's K ring).
-template <int NTH, size_t BYTES>
-struct SelectStage {
-  static constexpr int value = sizeof(SelectShared<NTH, 4096>) <= BYTES   ? 4096
-                               : sizeof(SelectShared<NTH, 2048>) <= BYTES ? 2048
-                                                                           : 1024;
-};
-
-template <int D, int NT, int W, bool PIPE, int RING, bool SEL>
+template <int D, int NT, int W, bool PIPE, int RING>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(UP_OCC_B)))
-up_colsum_kernel(ScoreArgs a, SelectArgs sa) {
+up_colsum_kernel(ScoreArgs a) {
   using Tile = KTile<D, W>;
   constexpr int KT = Tile::KT;
   __shared__ __attribute__((aligned(16))) uint16_t kl[RING][Tile::ELEMS];
   __shared__ float colbuf[2][W][64];
   constexpr int ROWS = NT * 32 * W;
   __shared__ float sbias[ROWS];
-  __shared__ uint32_t s_last;
 
   const Work wk = decode_work(a);
   if (!wk.valid) return;
@@ -1098,7 +1002,7 @@ up_colsum_kernel(ScoreArgs a, SelectArgs sa) {
       const int s0 = RING == kUnroll ? 0 : it % RING;
       ks.fetch_full(it + U + RING - 1, kl[(s0 + U + RING - 1) % RING]);
       if (it + U > 0)
-        colsum_flush<W, KT, true, SEL>(colbuf[(U + 1) & 1], wave, lane,
+        colsum_flush<W, KT, true>(colbuf[(U + 1) & 1], wave, lane,
                                        key0 + (it + U - 1) * KT, key1, colout);
       if constexpr (DB)
         colsum_iter_db<D, NT, W>(kl[(s0 + U) % RING], kl[(s0 + U + 1) % RING], key0 + (it + U) * KT,
@@ -1115,7 +1019,7 @@ up_colsum_kernel(ScoreArgs a, SelectArgs sa) {
       const bool more = it + RING - 1 < ntiles;
       if (more) ks.fetch(it + RING - 1, kl[(it + RING - 1) % RING]);
       if (it > 0)
-        colsum_flush<W, KT, false, SEL>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT,
+        colsum_flush<W, KT, false>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT,
                                         key1, colout);
       if constexpr (DB)
         colsum_iter_db<D, NT, W>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT, key1, lane,
@@ -1130,7 +1034,7 @@ up_colsum_kernel(ScoreArgs a, SelectArgs sa) {
   for (; it < ntiles; ++it) {
     if (it + RING - 1 < ntiles) ks.fetch(it + RING - 1, kl[(it + RING - 1) % RING]);
     if (it > 0)
-      colsum_flush<W, KT, false, SEL>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT,
+      colsum_flush<W, KT, false>(colbuf[(it + 1) & 1], wave, lane, key0 + (it - 1) * KT,
                                       key1, colout);
     f32x16_t acc = {};
     colsum_iter<D, NT, W, true, false>(kl[it % RING], kl[(it + 1) % RING], key0 + it * KT, key1,
@@ -1139,34 +1043,17 @@ up_colsum_kernel(ScoreArgs a, SelectArgs sa) {
     ring_step<RING, Tile, false>();
   }
   // the last tile (ntiles >= 1: the chunk holds at least one key)
-  colsum_flush<W, KT, false, SEL>(colbuf[(ntiles - 1) & 1], wave, lane,
+  colsum_flush<W, KT, false>(colbuf[(ntiles - 1) & 1], wave, lane,
                                   key0 + (ntiles - 1) * KT, key1, colout);
-
-  if constexpr (SEL) {
-    // Chunk epilogue, in the last of the chunk's workgroups to finish (one
-    // per KV head and row group holding rows of this request); the K ring's
-    // LDS is idle from here on.
-    const int rg_used = (R + ROWS - 1) / ROWS;
-    if (!arrive_last(&a.chunk_arrive[(int64_t)req * a.chunks_b + chunk],
-                     (uint32_t)(a.hkv * rg_used), s_last))
-      return;
-    static_assert(UP_CK_MAX * sizeof(float) <= sizeof(kl), "chunk scores fit the ring");
-    chunk_scores<64 * W>(a, req, s0, key0, key1, rg_used, reinterpret_cast<float*>(&kl[0][0]));
-    // the workgroup that completes the request's last chunk selects its blocks
-    const int nch = (L + a.ck - 1) / a.ck;
-    if (!arrive_last(&a.arrive[req], (uint32_t)nch, s_last)) return;
-    using Shared = SelectShared<64 * W, SelectStage<64 * W, sizeof(kl)>::value>;
-    static_assert(sizeof(Shared) <= sizeof(kl), "selection state fits the ring");
-    select_request<64 * W, Shared::kStage, true>(sa, req, *reinterpret_cast<Shared*>(&kl[0][0]));
-  }
 }
 
 // ---------------------------------------------------------------------------
 // Epilogue of up_score: token score = fixed-order sum of the per-(KV head,
 // row group) partials; block score = mean over the block's tokens.  One wave
-// per block.  (The fused entry point does the same in the column-sum
-// kernel's chunk epilogue, chunk_scores.)
+// per block.  The fused entry point runs the same code (COH: the block score
+// stored coherently) and selects in the same kernel.
 // ---------------------------------------------------------------------------
+template <bool COH>
 __device__ __forceinline__ void blockmean_one(const ScoreArgs& a, int64_t b, int lane) {
   // request owning block b: last r with cu_blocks[r] <= b
   int lo = 0, hi = a.num_seqs;  // invariant: cu_blocks[lo] <= b < cu_blocks[hi]
@@ -1192,13 +1079,69 @@ __device__ __forceinline__ void blockmean_one(const ScoreArgs& a, int64_t b, int
     sum += c;
   }
   sum = wave_sum_f32(sum);
-  if (lane == 0) a.block_scores[b] = sum / (float)(j1 - j0);
+  if (lane == 0) {
+    if constexpr (COH) store_coherent(&a.block_scores[b], sum / (float)(j1 - j0));
+    else a.block_scores[b] = sum / (float)(j1 - j0);
+  }
 }
 
 __global__ void __launch_bounds__(256) up_blockmean_kernel(ScoreArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * 4 + wave;
-  if (b < a.num_blocks) blockmean_one(a, b, lane);
+  if (b < a.num_blocks) blockmean_one<false>(a, b, lane);
+}
+
+// Count this workgroup in *counter once its coherent stores (store_coherent)
+// have completed; true, in every thread, in the workgroup that brings the
+// count to `expect`.  Every wave waits until its stores are acknowledged
+// (written through to memory) before the one thread counts, so the
+// workgroup that reads the final count finds every counted workgroup's
+// coherent stores with coherent loads.  No L2 write-back or invalidate.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expect, uint32_t& flag) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag = prev + 1 == expect ? 1u : 0u;
+  }
+  __syncthreads();
+  return flag != 0;
+}
+
+// Block means and the selection in one launch (up_score_select): one wave
+// per block as above, the block scores written coherently; each workgroup
+// then counts itself done for every request whose blocks it holds, and the
+// workgroup that completes a request selects its blocks (reading the scores
+// coherently), so the selection starts as soon as the request's last block
+// mean is written.
+__global__ void __launch_bounds__(kSelectThreads) up_blockmean_select_kernel(ScoreArgs a,
+                                                                             SelectArgs sa) {
+  constexpr int BPW = kSelectThreads / 64;  // blocks per workgroup
+  __shared__ SelectShared<kSelectThreads, kStageMax> sh;
+  __shared__ uint32_t s_last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b0 = (int64_t)blockIdx.x * BPW;
+  if (b0 + wave < a.num_blocks) blockmean_one<true>(a, b0 + wave, lane);
+  const int64_t b1 = min(b0 + BPW, a.num_blocks) - 1;
+  // requests owning the first and the last block here (the last r with
+  // cu_blocks[r] <= b); requests in between without blocks are skipped
+  auto owner = [&](int64_t b) {
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  const int r0 = owner(b0), r1 = owner(b1);
+  for (int r = r0; r <= r1; ++r) {  // uniform over the workgroup
+    const int64_t c0 = a.cu_blocks[r], c1 = a.cu_blocks[r + 1];
+    if (c1 == c0) continue;
+    const uint32_t wgs = (uint32_t)((c1 - 1) / BPW - c0 / BPW + 1);  // workgroups holding its blocks
+    if (arrive_last(&a.arrive[r], wgs, s_last))
+      select_request<kSelectThreads, kStageMax, true>(sa, r, sh);
+  }
 }
 
 // Compile-time tiling per head_dim and pass: NT 32-row tiles per wave, W
@@ -1308,7 +1251,7 @@ up_status launch_rowstats(const ScoreArgs& b_args, int rg_a, hipStream_t st) {
 
 template <int D>
 up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int ck_b,
-                        int64_t groups_b, const SelectArgs* sel, hipStream_t st) {
+                        int64_t groups_b, hipStream_t st) {
   using TB = typename Tiling<D>::B;
   up_status s = one_round_a ? launch_rowstats<D, typename Tiling<D>::A1>(b_args, rg_a, st)
                             : launch_rowstats<D, typename Tiling<D>::A>(b_args, rg_a, st);
@@ -1318,12 +1261,8 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int
   bb.ck = ck_b;
   bb.num_groups = groups_b;
   bb.reverse = UP_REVERSE_B;
-  if (sel)
-    hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE, TB::RING, true>),
-                       dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb, *sel);
-  else
-    hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE, TB::RING, false>),
-                       dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb, SelectArgs{});
+  hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE, TB::RING>),
+                     dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb);
   return check_launch("up_colsum_kernel");
 }
 
@@ -1464,10 +1403,6 @@ up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int h
   off = up::align_up(off + (size_t)hkv * g.rg * (size_t)T * sizeof(float), 256);
   g.off_arrive = off;
   off = up::align_up(off + (size_t)num_seqs * sizeof(uint32_t), 256);
-  // column-sum chunks hold at least 256 keys, whatever the block size
-  g.chunks_b = (int)std::max<int64_t>(1, up::ceil_div(max_len, 256));
-  g.off_chunk_arrive = off;
-  off = up::align_up(off + (size_t)num_seqs * g.chunks_b * sizeof(uint32_t), 256);
   g.bytes = off > 0 ? off : 256;
   out->g = g;
   out->bytes = g.bytes;
@@ -1589,11 +1524,8 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   a.block_scores = block_scores;
   a.num_blocks = N;
   a.arrive = reinterpret_cast<uint32_t*>(ws + lay.g.off_arrive);
-  a.chunk_arrive = reinterpret_cast<uint32_t*>(ws + lay.g.off_chunk_arrive);
-  a.chunks_b = lay.g.chunks_b;
   a.kept = sel ? sel->kept_tokens : nullptr;
-  // column-sum chunks hold whole blocks (the chunk epilogue averages them)
-  const int ck_b = (int)up::align_up((size_t)lay.g.ck_b, (size_t)block);
+  const int ck_b = lay.g.ck_b;
 
   a.num_groups = 0;
   int64_t groups_b = 0;
@@ -1604,23 +1536,26 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   const int64_t rgm = a.rg > lay.g.rg_a ? a.rg : lay.g.rg_a;
   const int64_t nwg = up::ceil_div(std::max(a.num_groups, groups_b), 8) * 8 * rgm;
   if (nwg > 0x7fffffff) return up::set_error(UP_ERR_UNSUPPORTED, "grid too large");
-  up::SelectArgs sa{};
-  if (sel)
-    sa = up::SelectArgs{cu_seqlens_d, cu_blocks_d, block_scores, sel->block_mask,
-                        sel->kept_tokens, block, sel->sink, sel->tail, sel->top_p};
-  const up::SelectArgs* sap = sel ? &sa : nullptr;
   switch (head_dim) {
     case 64:
-      st = up::launch_passes<64>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, sap, stream);
+      st = up::launch_passes<64>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, stream);
       break;
     case 128:
-      st = up::launch_passes<128>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, sap, stream);
+      st = up::launch_passes<128>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, stream);
       break;
     default:
-      st = up::launch_passes<256>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, sap, stream);
+      st = up::launch_passes<256>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, stream);
       break;
   }
-  if (st != UP_OK || sel) return st;
+  if (st != UP_OK) return st;
+  if (sel) {
+    const up::SelectArgs sa{cu_seqlens_d, cu_blocks_d, block_scores, sel->block_mask,
+                            sel->kept_tokens, block, sel->sink, sel->tail, sel->top_p};
+    hipLaunchKernelGGL(up::up_blockmean_select_kernel,
+                       dim3((unsigned)up::ceil_div(N, up::kSelectThreads / 64)),
+                       dim3(up::kSelectThreads), 0, stream, a, sa);
+    return up::check_launch("up_blockmean_select_kernel");
+  }
   hipLaunchKernelGGL(up::up_blockmean_kernel, dim3((unsigned)up::ceil_div(N, 4)), dim3(256), 0,
                      stream, a);
   return up::check_launch("up_blockmean_kernel");

@@ -1,6 +1,6 @@
 // Step 4 of the pruning path: Top-p block selection with forced blocks, one
 // workgroup per request (the rule and the algorithm are described in
-// up_select_impl.h, which the column-sum kernel of the fused entry point
+// up_select_impl.h, which the block-mean kernel of the fused entry point
 // shares).
 #include "up_select_impl.h"
 

@@ -32,8 +32,8 @@
 // A request with at most STAGE blocks has its keys and fixed-point masses
 // computed once into LDS (every later pass reads them there); longer requests
 // recompute them from the scores in memory on every pass.  The workgroup
-// size NTH and STAGE are template arguments, so the column-sum kernel can run
-// the selection with its own workgroup, its state in the K ring's LDS.
+// size NTH and STAGE are template arguments, so another kernel (the fused
+// entry point's block-mean kernel) can run the selection in its workgroups.
 // Fixed point differs from exact fp64 sums by < N * 2^-S of the top score, so
 // a decision can differ from an fp64 evaluation only when the cumulative
 // mass is within that distance of p * total.
@@ -158,7 +158,7 @@ __device__ void pick_bucket(Shared& sh, int buf, int shift, int width, uint64_t 
 
 // Block score i of a request: COHERENT reads it with a relaxed device-scope
 // atomic load, for scores written earlier in the same kernel by workgroups
-// on other XCDs (the column-sum kernel of the fused entry point).
+// on other XCDs (the block-mean kernel of the fused entry point).
 template <bool COHERENT>
 __device__ __forceinline__ float score_at(const float* sc, int i) {
   if constexpr (COHERENT)
