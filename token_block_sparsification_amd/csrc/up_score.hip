@@ -926,37 +926,25 @@ up_colsum_kernel(ScoreArgs a) {
         const int hl = rho / n_eff, ti = rho - hl * n_eff;
         const float2* pp = a.partial + ((int64_t)req * a.hq + g * a.rgqa + hl) * a.max_chunks *
                                            a.n_query + ti;
+        // Online merge, 32 partials in flight per round trip: the running sum
+        // is rescaled to each batch's larger maximum (by exp2(-inf) = 0 before
+        // the first batch, whose chunk 0 makes the maximum finite), so up to
+        // 32 chunks take one round trip and the sum is the plain one.
         float M = kNegInf, l = 0.f;
-        constexpr int CA = 32;  // up to 32 chunks: every partial in flight at once, read once
-        if (nch <= CA) {
-          float2 v[CA];
+        constexpr int CB = 32;
+        for (int c0 = 0; c0 < nch; c0 += CB) {
+          float2 v[CB];
 #pragma unroll
-          for (int u = 0; u < CA; ++u)
-            v[u] = u < nch ? pp[(int64_t)u * a.n_query] : make_float2(kNegInf, 0.f);
+          for (int u = 0; u < CB; ++u)
+            v[u] = c0 + u < nch ? pp[(int64_t)(c0 + u) * a.n_query] : make_float2(kNegInf, 0.f);
+          float bm = M;
 #pragma unroll
-          for (int u = 0; u < CA; ++u) M = fmaxf(M, v[u].x);
-          const float mc = M * C;
+          for (int u = 0; u < CB; ++u) bm = fmaxf(bm, v[u].x);
+          const float mc = bm * C;
+          l *= fast_exp2(fmaf(M, C, -mc));
 #pragma unroll
-          for (int u = 0; u < CA; ++u) l += v[u].y * fast_exp2(fmaf(v[u].x, C, -mc));
-        } else {
-          constexpr int CB = 8;  // partials loaded per batch (in flight together)
-          for (int c0 = 0; c0 < nch; c0 += CB) {
-            float x[CB];
-#pragma unroll
-            for (int u = 0; u < CB; ++u)
-              x[u] = c0 + u < nch ? pp[(int64_t)(c0 + u) * a.n_query].x : kNegInf;
-#pragma unroll
-            for (int u = 0; u < CB; ++u) M = fmaxf(M, x[u]);
-          }
-          const float mc = M * C;
-          for (int c0 = 0; c0 < nch; c0 += CB) {
-            float2 v[CB];
-#pragma unroll
-            for (int u = 0; u < CB; ++u)
-              v[u] = c0 + u < nch ? pp[(int64_t)(c0 + u) * a.n_query] : make_float2(kNegInf, 0.f);
-#pragma unroll
-            for (int u = 0; u < CB; ++u) l += v[u].y * fast_exp2(fmaf(v[u].x, C, -mc));
-          }
+          for (int u = 0; u < CB; ++u) l += v[u].y * fast_exp2(fmaf(v[u].x, C, -mc));
+          M = bm;
         }
         b = M * C + log2f(l);
       }
