@@ -16,8 +16,8 @@ from _parity import GpuRun, check_compaction, check_mask, check_scores, oracle_q
 pytestmark = pytest.mark.gpu
 
 
-def _full(name, **over):
-    w = W.get_workload(name)
+def _full(base, **over):
+    w = W.get_workload(base)
     if over:
         w = w.with_(**over)
     dev = torch.device("cuda")
@@ -62,6 +62,17 @@ def test_llama_shapes(name):
 
 def test_packed_batch16():
     _full("llama8b_batch16")
+
+
+@pytest.mark.parametrize("log2_len", [20, 22])
+def test_long_request_beyond_the_benchmark(log2_len):
+    """One 2^20- or 2^22-token request and a short one (head_dim 64, 4/4
+    heads): the row statistics run 256 / 1024 key chunks per row that the
+    column-sum prologue merges, the request has 16,384 / 65,536 blocks (a
+    selection that does not stage them in LDS) and the compaction scans 17 /
+    65 tiles; token offsets reach 2^28 elements of K."""
+    L = 1 << log2_len
+    _full("small_L2048", name=f"long_L{L}", lengths=(L, 3000), num_seqs=2, hidden_dim=64)
 
 
 @pytest.mark.parametrize("n", [32, 128, 512])
