@@ -70,6 +70,47 @@ def test_n_and_block_sweep(n, G):
     _end_to_end(W.make_inputs(w), n, G, name=w.name)
 
 
+@pytest.mark.parametrize("G", [1, 4096])
+def test_select_and_compact_at_block_size_limits(G):
+    """Selection and compaction at the smallest and largest block the two
+    calls accept (scoring takes powers of two in [16, 256], both ends in the
+    sweep above): every token its own block (a 20,000-block request,
+    selected without LDS staging; one copy descriptor per token) and
+    4096-token blocks (requests of one to five blocks, most of them forced),
+    with an empty request between, on seeded block scores: masks and kept
+    counts equal the oracle's, the compaction bit for bit."""
+    dev = torch.device("cuda")
+    lens = [9000, 777, 0, 20000]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    batch = U.Batch.make(torch.from_numpy(cu), G, dev)
+    T, N = batch.num_tokens, batch.num_blocks
+    sc = W.gen.make_scores(7100 + G, N).numpy()
+    bs = torch.from_numpy(sc).to(dev)
+    gen = torch.Generator().manual_seed(G)
+    hidden = torch.randint(-1000, 1000, (T, 24), dtype=torch.int32, generator=gen).to(dev)
+    pos = (torch.arange(T, dtype=torch.int32) * 2 + 1).to(dev)
+    ws = U.new_compact_workspace(batch.cu_seqlens_h, G, dev)
+    for p, sink, tail in [(0.9, 64, 64), (0.5, 0, 0)]:
+        mask = torch.empty(N, dtype=torch.uint8, device=dev)
+        kept = torch.empty(len(lens), dtype=torch.int32, device=dev)
+        U.up_select_topp(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, bs, G, p, sink,
+                         tail, mask, kept)
+        out = torch.zeros_like(hidden)
+        pout = torch.full_like(pos, -1)
+        cu_out = torch.empty(len(lens) + 1, dtype=torch.int32, device=dev)
+        U.up_compact(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, G, mask, hidden,
+                     pos, out, pout, cu_out, ws)
+        torch.cuda.synchronize()
+        ref_m, ref_k = O.select_topp(sc.astype(np.float64), cu, G, p, sink, tail)
+        assert np.array_equal(mask.cpu().numpy(), ref_m), (G, p)
+        assert list(kept.cpu().numpy()) == list(ref_k)
+        exp_h, exp_p, exp_cu = O.compact(ref_m, hidden.cpu().numpy(), pos.cpu().numpy(), cu, G)
+        n = int(exp_cu[-1])
+        assert cu_out.cpu().tolist() == list(exp_cu)
+        assert np.array_equal(out[:n].cpu().numpy(), exp_h) and (out[n:] == 0).all()
+        assert np.array_equal(pout[:n].cpu().numpy(), exp_p) and (pout[n:] == -1).all()
+
+
 @pytest.mark.parametrize("n,G,d", [(4096, 64, 128), (700, 16, 64), (96, 256, 128)])
 def test_large_n_and_head_dims(n, G, d):
     """n up to the 4096 limit (requests shorter and longer than n), with the
