@@ -400,6 +400,38 @@ def test_compact_workspace_across_batch_sizes():
         assert not ws.view(torch.int32)[:2].any() and not ws[256:256 + 8 * tiles].any()
 
 
+@pytest.mark.parametrize("lens", [[0, 0, 0], []], ids=["all_empty", "no_requests"])
+def test_scoring_and_selection_of_empty_batches(lens):
+    """A batch of empty requests (T = 0) and a batch of none: up_score and
+    up_select_topp write nothing, every kept count is 0 (up_score_select
+    writes them with its own small kernel), and no output is touched past its
+    (empty) extent."""
+    dev = torch.device("cuda")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    batch = U.Batch.make(cu, 64, dev)
+    B = batch.num_seqs
+    q = torch.empty((0, 4, 64), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((0, 4, 64), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(U.up_score_workspace_size(batch.cu_seqlens_h, 4, 4, 64, 128),
+                     dtype=torch.uint8, device=dev)
+    sentinel = torch.full((4,), 7.0, device=dev)
+    mask = torch.full((4,), 9, dtype=torch.uint8, device=dev)
+    for call in ("unfused", "fused"):
+        kept = torch.full((B + 1,), 5, dtype=torch.int32, device=dev)
+        if call == "unfused":
+            U.up_score(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, q, k, 128, 64,
+                       0.0, sentinel[:0], sentinel[:0], ws)
+            U.up_select_topp(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d,
+                             sentinel[:0], 64, 0.99, 128, 128, mask[:0], kept[:B])
+        else:
+            U.up_score_select(batch.cu_seqlens_h, batch.cu_seqlens_d, batch.cu_blocks_d, q, k, 128,
+                              64, 0.0, sentinel[:0], sentinel[:0], 0.99, 128, 128, mask[:0],
+                              kept[:B], ws)
+        torch.cuda.synchronize()
+        assert kept.tolist() == [0] * B + [5], call
+        assert (sentinel == 7.0).all() and (mask == 9).all(), call
+
+
 def test_compact_all_empty_and_no_positions():
     dev = torch.device("cuda")
     cu = torch.tensor([0, 0, 0, 0], dtype=torch.int32)
