@@ -1057,12 +1057,26 @@ __device__ __forceinline__ void blockmean_one(const ScoreArgs& a, int64_t b, int
   // only the row groups that hold rows of this request wrote partials
   const int n_eff = min(a.n_query, L);
   const int rg_used = (a.rgqa * n_eff + a.rows_per_wg - 1) / a.rows_per_wg;
+  const int nterm = a.hkv * rg_used;
   float sum = 0.f;
   for (int j = j0 + lane; j < j1; j += 64) {
+    // Terms in (KV head, row group) order, g-major: eight loads are issued
+    // before the first is added, so a token takes one round trip per eight
+    // terms instead of one per term; the additions keep that order.
+    const float* p = a.colpart + s0 + j;
     float c = 0.f;
-    for (int g = 0; g < a.hkv; ++g)
-      for (int rgi = 0; rgi < rg_used; ++rgi)
-        c += a.colpart[((int64_t)g * a.rg + rgi) * a.T + s0 + j];
+    int g = 0, rgi = 0;
+    for (int t0 = 0; t0 < nterm; t0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v[u] = t0 + u < nterm ? p[((int64_t)g * a.rg + rgi) * a.T] : 0.f;
+        if (++rgi == rg_used) { rgi = 0; ++g; }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (t0 + u < nterm) c += v[u];
+    }
     if (a.token_scores) a.token_scores[s0 + j] = c;
     sum += c;
   }
