@@ -182,24 +182,58 @@ __global__ void __launch_bounds__(NTH) up_compact_scan_kernel(CompactArgs a) {
   if (ONE || t < a.num_tiles) {
     // This thread's blocks: kScanPerThread consecutive ones.
     const int64_t b0 = t * kTileBlocks + (int64_t)tid * kScanPerThread;
-    int req[kScanPerThread], rows[kScanPerThread];
+    int req[kScanPerThread], rows[kScanPerThread], src[kScanPerThread];
+    bool ends[kScanPerThread];
     int64_t kept[kScanPerThread];
     int64_t mine = 0;
-    int r = b0 < a.num_blocks ? block_request(a.cu_blocks, a.num_seqs, b0) : 0;
+    if (b0 < a.num_blocks) {
+      // The mask bytes and the first block's request bounds are loaded
+      // together (one round trip); a thread's blocks rarely cross a request
+      // boundary, and only then does it load the next request's bounds.
+      int r = block_request(a.cu_blocks, a.num_seqs, b0);
+      int cb_lo = a.cu_blocks[r], cb_hi = a.cu_blocks[r + 1];
+      int s_lo = a.cu_seqlens[r], s_hi = a.cu_seqlens[r + 1];
+      uint8_t mk[kScanPerThread];
+      if (b0 + kScanPerThread <= a.num_blocks) {  // straight-line loads, one wait
 #pragma unroll
-    for (int i = 0; i < kScanPerThread; ++i) {
-      const int64_t b = b0 + i;
-      req[i] = -1;
-      rows[i] = 0;
-      kept[i] = 0;
-      if (b < a.num_blocks) {
-        while (a.cu_blocks[r + 1] <= b) ++r;  // skip to the owning request
-        const int L = a.cu_seqlens[r + 1] - a.cu_seqlens[r];
-        const int lb = (int)(b - a.cu_blocks[r]);
-        req[i] = r;
-        rows[i] = min(lb * a.block + a.block, L) - lb * a.block;
-        kept[i] = a.mask[b] ? rows[i] : 0;
-        mine += kept[i];
+        for (int i = 0; i < kScanPerThread; ++i) mk[i] = a.mask[b0 + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < kScanPerThread; ++i) mk[i] = b0 + i < a.num_blocks ? a.mask[b0 + i] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < kScanPerThread; ++i) {
+        const int64_t b = b0 + i;
+        req[i] = -1;
+        rows[i] = 0;
+        src[i] = 0;
+        ends[i] = false;
+        kept[i] = 0;
+        if (b < a.num_blocks) {
+          while (cb_hi <= b) {  // skip to the owning request
+            ++r;
+            cb_lo = cb_hi;
+            cb_hi = a.cu_blocks[r + 1];
+            s_lo = s_hi;
+            s_hi = a.cu_seqlens[r + 1];
+          }
+          const int lb = (int)(b - cb_lo);
+          req[i] = r;
+          rows[i] = min(lb * a.block + a.block, s_hi - s_lo) - lb * a.block;
+          src[i] = s_lo + lb * a.block;
+          ends[i] = b == cb_hi - 1;
+          kept[i] = mk[i] ? rows[i] : 0;
+          mine += kept[i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kScanPerThread; ++i) {
+        req[i] = -1;
+        rows[i] = 0;
+        src[i] = 0;
+        ends[i] = false;
+        kept[i] = 0;
       }
     }
     // Exclusive scan of the threads' kept rows: waves, then across waves.
@@ -266,13 +300,13 @@ __global__ void __launch_bounds__(NTH) up_compact_scan_kernel(CompactArgs a) {
       const int rq = req[i];
       BlockCopy d;
       d.dst = (kept[i] > 0 && pos + kept[i] <= a.capacity) ? pos : -1;  // never past the output
-      d.src = a.cu_seqlens[rq] + (int)(b - a.cu_blocks[rq]) * a.block;
+      d.src = src[i];
       d.rows = rows[i];
       a.desc[b] = d;
       pos += kept[i];
       // A request whose last block this is (and empty requests right after
       // it) ends at this block's inclusive count.
-      if (a.cu_out && b == a.cu_blocks[rq + 1] - 1) {
+      if (a.cu_out && ends[i]) {
         a.cu_out[rq + 1] = (int32_t)pos;
         for (int r2 = rq + 1; r2 < a.num_seqs && a.cu_blocks[r2 + 1] == a.cu_blocks[rq + 1]; ++r2)
           a.cu_out[r2 + 1] = (int32_t)pos;

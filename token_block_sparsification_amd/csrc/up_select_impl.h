@@ -183,8 +183,7 @@ __device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared<N
   // 1. largest score, smallest / largest optional key (staging the scores)
   float mx = 0.f;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int i = tid; i < nb; i += kSelectThreads) {
-    const float s = score_at<COHERENT>(sc, i);
+  auto visit = [&](int i, float s) {
     if (STAGED) sh.skey[i] = __float_as_uint(s);
     mx = fmaxf(mx, s);
     if (!is_forced(i, L, G, a.sink, a.tail)) {
@@ -192,6 +191,24 @@ __device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared<N
       kmin = min(kmin, k);
       kmax = max(kmax, k);
     }
+  };
+  if constexpr (STAGED) {
+    // at most STAGE / NTH scores per thread: all loads issued before the
+    // first is used (one round trip instead of one per score)
+    constexpr int PER = (STAGE + kSelectThreads - 1) / kSelectThreads;
+    float v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kSelectThreads;
+      v[u] = i < nb ? score_at<COHERENT>(sc, i) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kSelectThreads;
+      if (i < nb) visit(i, v[u]);
+    }
+  } else {
+    for (int i = tid; i < nb; i += kSelectThreads) visit(i, score_at<COHERENT>(sc, i));
   }
   mx = __uint_as_float(wave_allreduce32(__float_as_uint(mx), [](uint32_t a, uint32_t b) {
     return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
