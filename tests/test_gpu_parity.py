@@ -173,6 +173,33 @@ def test_blocks_straddling_column_sum_chunks(G):
     _end_to_end(W.make_inputs(w), 128, G, name=w.name)
 
 
+def _many_lengths(kind):
+    rng = np.random.default_rng({"one_chunk": 71, "windows": 72}[kind])
+    if kind == "one_chunk":
+        # every request holds 1..200 keys: one key chunk each
+        return tuple(int(x) for x in rng.integers(1, 201, size=300))
+    # empty requests, short ones and a few long ones: several 64-request windows
+    lens = [int(x) for x in rng.integers(0, 400, size=150)]
+    for i in (0, 37, 64, 65, 128, 149):
+        lens[i] = 0
+    for i in (5, 70, 140):
+        lens[i] = 5000 + i
+    return tuple(lens)
+
+
+@pytest.mark.parametrize("kind", ["one_chunk", "windows"])
+def test_many_requests(kind):
+    """Batches of 150-300 requests: the scoring kernels find a workgroup's
+    request directly when every request is one key chunk, else by scanning
+    64 requests per step; requests at window edges (63/64, 127/128), empty
+    requests inside and at the ends of windows, long requests in between."""
+    lengths = _many_lengths(kind)
+    w = W.Workload(name=f"many_{kind}", lengths=lengths, hq=8, hkv=2, head_dim=128,
+                   hidden_dim=64, hidden_dtype="bf16", seed=6200 + len(lengths), plant_frac=0.05,
+                   num_seqs=len(lengths))
+    _end_to_end(W.make_inputs(w), 128, 64, name=w.name)
+
+
 def test_tail_equals_n_and_small_p():
     w = W.Workload(name="p_sweep", lengths=(4096, 2000), hq=8, hkv=2, head_dim=128, hidden_dim=32,
                    hidden_dtype="bf16", seed=6001, plant_frac=0.1, num_seqs=2)

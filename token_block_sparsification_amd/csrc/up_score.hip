@@ -81,6 +81,7 @@ struct ScoreArgs {
   int ck_a;           // keys per row-statistics chunk (the partials' chunking)
   int64_t num_groups;  // real (request, KV head, key chunk) groups
   int reverse;         // walk the groups last to first
+  int one_chunk;       // every request holds 1..ck keys: request = group / hkv
   float c;  // scale * log2(e)
   float2* partial;  // [B][hq][max_chunks][n_query] (raw max, sum of exp2)
   float* colpart;   // [hkv * rg][T]
@@ -129,6 +130,11 @@ struct Work {
   bool valid;
 };
 
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), lane) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+}
+
 __device__ __forceinline__ Work decode_work(const ScoreArgs& a) {
   const int64_t w = blockIdx.x;
   const int64_t span = 8 * (int64_t)a.rg;
@@ -142,19 +148,45 @@ __device__ __forceinline__ Work decode_work(const ScoreArgs& a) {
   wk.g = 0;
   wk.chunk = 0;
   if (!wk.valid) return wk;
-  // find the request holding group q (uniform scalar loop over requests)
-  int r = 0;
-  for (; r < a.num_seqs; ++r) {
-    const int L = a.cu_seqlens[r + 1] - a.cu_seqlens[r];
-    const int64_t ng = (int64_t)((L + a.ck - 1) / a.ck) * a.hkv;
-    if (q < ng) break;
-    q -= ng;
+  if (a.one_chunk) {  // hkv groups per request, in request order
+    const int r = (int)(q / a.hkv);
+    wk.req = r;
+    wk.g = (int)(q - (int64_t)r * a.hkv);
+    return wk;
   }
+  // Find the request holding group q, 64 requests per step (one per lane):
+  // a wave-wide inclusive scan of their group counts, then the first lane
+  // whose prefix passes q.  A batch of B requests costs ceil(B / 64) round
+  // trips instead of B dependent ones.
+  const int lane = threadIdx.x & 63;
+  int r = -1;
+  for (int r0 = 0; r0 < a.num_seqs; r0 += 64) {
+    const int rr = r0 + lane;
+    uint64_t ng = 0;
+    if (rr < a.num_seqs) {
+      const int L = a.cu_seqlens[rr + 1] - a.cu_seqlens[rr];
+      ng = (uint64_t)((L + a.ck - 1) / a.ck) * (uint64_t)a.hkv;
+    }
+    const uint64_t incl = wave_scan_incl(ng);
+    const uint64_t total = readlane64(incl, 63);
+    if ((uint64_t)q < total) {
+      const int owner = __ffsll((unsigned long long)__ballot(incl > (uint64_t)q)) - 1;
+      q -= (int64_t)readlane64(incl - ng, owner);
+      r = r0 + owner;
+      break;
+    }
+    q -= (int64_t)total;
+  }
+  if (r < 0) {  // only if the device cu_seqlens disagree with the host copy
+    wk.valid = false;
+    return wk;
+  }
+  r = __builtin_amdgcn_readfirstlane(r);
   const int L = a.cu_seqlens[r + 1] - a.cu_seqlens[r];
   const int nch = (L + a.ck - 1) / a.ck;
   wk.req = r;
-  wk.g = (int)(q / nch);
-  wk.chunk = (int)(q - (int64_t)wk.g * nch);
+  wk.g = __builtin_amdgcn_readfirstlane((int)(q / nch));
+  wk.chunk = __builtin_amdgcn_readfirstlane((int)(q - (int64_t)wk.g * nch));
   return wk;
 }
 
@@ -1263,7 +1295,7 @@ up_status launch_rowstats(const ScoreArgs& b_args, int rg_a, hipStream_t st) {
 
 template <int D>
 up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int ck_b,
-                        int64_t groups_b, hipStream_t st) {
+                        int64_t groups_b, int one_chunk_b, hipStream_t st) {
   using TB = typename Tiling<D>::B;
   up_status s = one_round_a ? launch_rowstats<D, typename Tiling<D>::A1>(b_args, rg_a, st)
                             : launch_rowstats<D, typename Tiling<D>::A>(b_args, rg_a, st);
@@ -1272,6 +1304,7 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int
   bb.ck_a = b_args.ck;
   bb.ck = ck_b;
   bb.num_groups = groups_b;
+  bb.one_chunk = one_chunk_b;
   bb.reverse = UP_REVERSE_B;
   hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE, TB::RING>),
                      dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb);
@@ -1541,22 +1574,31 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
 
   a.num_groups = 0;
   int64_t groups_b = 0;
+  bool one_a = true, one_b = true;
   for (int r = 0; r < num_seqs; ++r) {
-    a.num_groups += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], a.ck) * (int64_t)hkv;
-    groups_b += up::ceil_div(cu_seqlens_h[r + 1] - cu_seqlens_h[r], ck_b) * (int64_t)hkv;
+    const int L = cu_seqlens_h[r + 1] - cu_seqlens_h[r];
+    a.num_groups += up::ceil_div(L, a.ck) * (int64_t)hkv;
+    groups_b += up::ceil_div(L, ck_b) * (int64_t)hkv;
+    one_a = one_a && L >= 1 && L <= a.ck;
+    one_b = one_b && L >= 1 && L <= ck_b;
   }
+  a.one_chunk = one_a ? 1 : 0;
+  const int one_chunk_b = one_b ? 1 : 0;
   const int64_t rgm = a.rg > lay.g.rg_a ? a.rg : lay.g.rg_a;
   const int64_t nwg = up::ceil_div(std::max(a.num_groups, groups_b), 8) * 8 * rgm;
   if (nwg > 0x7fffffff) return up::set_error(UP_ERR_UNSUPPORTED, "grid too large");
   switch (head_dim) {
     case 64:
-      st = up::launch_passes<64>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, stream);
+      st = up::launch_passes<64>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, one_chunk_b,
+                                   stream);
       break;
     case 128:
-      st = up::launch_passes<128>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, stream);
+      st = up::launch_passes<128>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, one_chunk_b,
+                                   stream);
       break;
     default:
-      st = up::launch_passes<256>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, stream);
+      st = up::launch_passes<256>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, one_chunk_b,
+                                   stream);
       break;
   }
   if (st != UP_OK) return st;
