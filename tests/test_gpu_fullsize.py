@@ -64,6 +64,12 @@ def test_packed_batch16():
     _full("llama8b_batch16")
 
 
+def test_many_short_requests():
+    """256 requests of 512 tokens: 2048 scoring workgroups over several
+    resident rounds, each request one key chunk."""
+    _full("llama8b_batch256_L512")
+
+
 @pytest.mark.parametrize("log2_len", [20, 22])
 def test_long_request_beyond_the_benchmark(log2_len):
     """One 2^20- or 2^22-token request and a short one (head_dim 64, 4/4

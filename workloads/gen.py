@@ -166,6 +166,11 @@ WORKLOADS = {
         hidden_dim=4096, hidden_dtype="bf16", seed=1005, plant_frac=0.05,
         description="16 packed requests, lengths log-uniform in [4096, 131072], "
                     "Llama-3.1-8B shapes, 5% planted blocks per request"),
+    "llama8b_batch256_L512": Workload(
+        name="llama8b_batch256_L512", lengths=(512,) * 256, num_seqs=256, hq=32, hkv=8,
+        head_dim=128, hidden_dim=4096, hidden_dtype="bf16", seed=1006, plant_count=1,
+        description="256 packed requests of 512 tokens (131,072 in all), Llama-3.1-8B shapes, "
+                    "one planted block per request"),
 }
 for _i_n in range(3):
     for _i_g in range(3):
