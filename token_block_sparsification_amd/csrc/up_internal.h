@@ -34,6 +34,7 @@ struct ScoreGeometry {
   int rg_a;          // row-statistics row groups per KV head (of the tiling in use)
   int rg_a1;         // the same for pass A's one-round tiling
   int one_round_a;   // pass A runs its one-round tiling
+  int rounds_b;      // pass B runs its several-rounds tiling (rows_per_wg and rg are its)
   int ck;            // keys per row-statistics workgroup chunk (sets the partials layout)
   int ck_b;          // keys per column-sum workgroup chunk
   int max_chunks;    // chunks of the longest request
@@ -44,9 +45,11 @@ ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int h
                              int head_dim, int n_query);
 
 // Workgroups of a scoring pass resident at once (pass 0: row statistics,
-// 1: row statistics in its one-round tiling, 2: column sums).
+// 1: row statistics in its one-round tiling, 2: column sums, 3: column sums
+// in their several-rounds tiling).
 int resident_wgs_for(int head_dim, int pass);
 bool has_one_round_tiling(int head_dim);
+bool has_rounds_tiling_b(int head_dim);
 
 // Number of blocks a compaction tile spans for block size G.
 int compact_tile_blocks(int block);

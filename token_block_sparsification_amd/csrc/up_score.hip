@@ -1232,6 +1232,22 @@ __global__ void __launch_bounds__(kSelectThreads) up_blockmean_select_kernel(Sco
 #ifndef UP_TILE_B256
 #define UP_TILE_B256 1, 8, true, 4
 #endif
+// Pass B when the batch needs several resident rounds: two 4-wave workgroups
+// per CU at head_dim 128, so that one workgroup's prologue (query rows, first
+// K tiles, the merge of its rows' chunk partials) overlaps the other's key
+// loop (same box, per up_score: 256 requests of 512 tokens 415-419 vs 433-440
+// us, the 16-request batch 1144-1148 vs 1148-1163 us; a single 128K request,
+// one round, keeps the 8-wave form: 267.5 vs 272.3 us with the 4-wave one).
+// Head_dim 64 and 256 keep their one tiling.
+#ifndef UP_TILE_B64_ROUNDS
+#define UP_TILE_B64_ROUNDS UP_TILE_B64
+#endif
+#ifndef UP_TILE_B128_ROUNDS
+#define UP_TILE_B128_ROUNDS 2, 4, true, 4
+#endif
+#ifndef UP_TILE_B256_ROUNDS
+#define UP_TILE_B256_ROUNDS UP_TILE_B256
+#endif
 template <int NT_, int W_, bool PIPE_, int RING_>
 struct TileCfg {
   static constexpr int NT = NT_, W = W_, RING = RING_;
@@ -1239,32 +1255,36 @@ struct TileCfg {
   static constexpr int ROWS = NT * 32 * W;
 };
 template <int D> struct Tiling;
-// A1: the pass-A tiling for a batch that fits one resident round of it.
+// A1: the pass-A tiling for a batch that fits one resident round of it;
+// BR: the pass-B tiling for a batch that needs several rounds of B.
 template <> struct Tiling<64> {
   using A = TileCfg<UP_TILE_A64>;
   using A1 = TileCfg<UP_TILE_A64_ONE_ROUND>;
   using B = TileCfg<UP_TILE_B64>;
+  using BR = TileCfg<UP_TILE_B64_ROUNDS>;
 };
 template <> struct Tiling<128> {
   using A = TileCfg<UP_TILE_A128>;
   using A1 = TileCfg<UP_TILE_A128_ONE_ROUND>;
   using B = TileCfg<UP_TILE_B128>;
+  using BR = TileCfg<UP_TILE_B128_ROUNDS>;
 };
 template <> struct Tiling<256> {
   using A = TileCfg<UP_TILE_A256>;
   using A1 = TileCfg<UP_TILE_A256_ONE_ROUND>;
   using B = TileCfg<UP_TILE_B256>;
+  using BR = TileCfg<UP_TILE_B256_ROUNDS>;
 };
 
 // Rows and waves per workgroup of pass A (pass 0), pass A's one-round
-// tiling (pass 1) and pass B (pass 2).
+// tiling (pass 1), pass B (pass 2) and pass B's several-rounds tiling (3).
 template <typename T>
 int tiling_rows(int pass) {
-  return pass == 0 ? T::A::ROWS : pass == 1 ? T::A1::ROWS : T::B::ROWS;
+  return pass == 0 ? T::A::ROWS : pass == 1 ? T::A1::ROWS : pass == 2 ? T::B::ROWS : T::BR::ROWS;
 }
 template <typename T>
 int tiling_waves(int pass) {
-  return pass == 0 ? T::A::W : pass == 1 ? T::A1::W : T::B::W;
+  return pass == 0 ? T::A::W : pass == 1 ? T::A1::W : pass == 2 ? T::B::W : T::BR::W;
 }
 int rows_per_wg_for(int d, int pass) {
   switch (d) {
@@ -1293,10 +1313,16 @@ up_status launch_rowstats(const ScoreArgs& b_args, int rg_a, hipStream_t st) {
   return check_launch("up_rowstats_kernel");
 }
 
+template <int D, typename TB>
+up_status launch_colsum(const ScoreArgs& bb, hipStream_t st) {
+  hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE, TB::RING>),
+                     dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb);
+  return check_launch("up_colsum_kernel");
+}
+
 template <int D>
-up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int ck_b,
-                        int64_t groups_b, int one_chunk_b, hipStream_t st) {
-  using TB = typename Tiling<D>::B;
+up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, bool rounds_b,
+                        int ck_b, int64_t groups_b, int one_chunk_b, hipStream_t st) {
   up_status s = one_round_a ? launch_rowstats<D, typename Tiling<D>::A1>(b_args, rg_a, st)
                             : launch_rowstats<D, typename Tiling<D>::A>(b_args, rg_a, st);
   if (s != UP_OK) return s;
@@ -1306,9 +1332,8 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int
   bb.num_groups = groups_b;
   bb.one_chunk = one_chunk_b;
   bb.reverse = UP_REVERSE_B;
-  hipLaunchKernelGGL((up_colsum_kernel<D, TB::NT, TB::W, TB::PIPE, TB::RING>),
-                     dim3((unsigned)grid_for(bb)), dim3(64 * TB::W), 0, st, bb);
-  return check_launch("up_colsum_kernel");
+  return rounds_b ? launch_colsum<D, typename Tiling<D>::BR>(bb, st)
+                  : launch_colsum<D, typename Tiling<D>::B>(bb, st);
 }
 
 }  // namespace
@@ -1320,8 +1345,16 @@ up_status launch_passes(const ScoreArgs& b_args, int rg_a, bool one_round_a, int
 #define UP_NUM_CUS 256
 #endif
 int resident_wgs_for(int d, int pass) {
-  const int waves_per_cu = 4 * (pass == 2 ? UP_OCC_B : UP_OCC_A);
+  const int waves_per_cu = 4 * (pass >= 2 ? UP_OCC_B : UP_OCC_A);
   return UP_NUM_CUS * std::max(1, waves_per_cu / waves_per_wg_for(d, pass));
+}
+
+bool has_rounds_tiling_b(int d) {
+  switch (d) {
+    case 64: return !std::is_same<Tiling<64>::B, Tiling<64>::BR>::value;
+    case 128: return !std::is_same<Tiling<128>::B, Tiling<128>::BR>::value;
+    default: return !std::is_same<Tiling<256>::B, Tiling<256>::BR>::value;
+  }
 }
 
 bool has_one_round_tiling(int d) {
@@ -1344,6 +1377,7 @@ ScoreGeometry score_geometry(int num_seqs, int64_t T, int max_len, int hq, int h
   const int rows_a1 = rows_per_wg_for(head_dim, 1);
   g.rg_a1 = (int)(rmax > 0 ? ceil_div(rmax, rows_a1) : 1);
   g.one_round_a = 0;
+  g.rounds_b = 0;
   g.ck = 0;  // chosen by the caller once lengths are known
   g.max_chunks = 0;
   (void)num_seqs;
@@ -1440,6 +1474,20 @@ up_status score_layout(int num_seqs, const int32_t* cu_h, int hq, int hkv, int h
     }
   }
   g.ck_b = choose_ck_rounds(num_seqs, cu_h, hkv, g.rg, up::resident_wgs_for(head_dim, 2), g.ck);
+  if (up::has_rounds_tiling_b(head_dim)) {
+    // pass B's several-rounds tiling when its own tiling needs more than one round
+    int64_t wgs_b = 0;
+    for (int r = 0; r < num_seqs; ++r)
+      wgs_b += up::ceil_div(cu_h[r + 1] - cu_h[r], g.ck_b) * (int64_t)hkv * g.rg;
+    if (wgs_b > up::resident_wgs_for(head_dim, 2)) {
+      const int64_t rmax = (int64_t)(hq / hkv) * std::min(n_query, max_len);
+      g.rounds_b = 1;
+      g.rows_per_wg = up::rows_per_wg_for(head_dim, 3);
+      g.rg = (int)(rmax > 0 ? up::ceil_div(rmax, g.rows_per_wg) : 1);
+      g.ck_b = choose_ck_rounds(num_seqs, cu_h, hkv, g.rg, up::resident_wgs_for(head_dim, 3),
+                                g.ck);
+    }
+  }
   g.max_chunks = (int)(max_len > 0 ? up::ceil_div(max_len, g.ck) : 1);
   size_t off = 0;
   g.off_partial = off;
@@ -1589,15 +1637,18 @@ up_status score_call(int num_seqs, const int32_t* cu_seqlens_h, const int32_t* c
   if (nwg > 0x7fffffff) return up::set_error(UP_ERR_UNSUPPORTED, "grid too large");
   switch (head_dim) {
     case 64:
-      st = up::launch_passes<64>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, one_chunk_b,
+      st = up::launch_passes<64>(a, lay.g.rg_a, lay.g.one_round_a, lay.g.rounds_b, ck_b, groups_b,
+                                   one_chunk_b,
                                    stream);
       break;
     case 128:
-      st = up::launch_passes<128>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, one_chunk_b,
+      st = up::launch_passes<128>(a, lay.g.rg_a, lay.g.one_round_a, lay.g.rounds_b, ck_b, groups_b,
+                                   one_chunk_b,
                                    stream);
       break;
     default:
-      st = up::launch_passes<256>(a, lay.g.rg_a, lay.g.one_round_a, ck_b, groups_b, one_chunk_b,
+      st = up::launch_passes<256>(a, lay.g.rg_a, lay.g.one_round_a, lay.g.rounds_b, ck_b, groups_b,
+                                   one_chunk_b,
                                    stream);
       break;
   }
