@@ -88,7 +88,7 @@ def load_traffic(kernel: str, src: str, workload: str):
 
 
 COPY_BYTES = 1 << 30
-EVENT_EVERY = 4  # timed steps per bracketed dominant call
+EVENT_EVERY = 10  # timed steps per bracketed dominant call
 # name in traffic.json -> (source file, pattern of the dispatch names it covers)
 TRAFFIC_KERNELS = {
     "up_compact_copy_kernel": ("up_compact.hip", r"\bup_compact_copy_kernel<\d+, false>"),
@@ -253,7 +253,9 @@ def main():
     # copy kernel alone (events the library records right around its launch,
     # up_set_copy_events); the larger of them over the timed region is the
     # dominant one.  Each event record leaves the GPU idle for ~5 us, so
-    # bracketing every step would add ~11 us per piece bracketed.
+    # bracketing every step would add ~11 us per piece bracketed; one step in
+    # ten adds ~2 us per step on average and still averages 10 launches of
+    # each piece over a 100-step run.
     K = args.steps
     big = ("up_score", "copy_kernel")
     sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
