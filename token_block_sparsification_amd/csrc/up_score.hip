@@ -1073,15 +1073,27 @@ up_colsum_kernel(ScoreArgs a) {
 // per block.  The fused entry point runs the same code (COH: the block score
 // stored coherently) and selects in the same kernel.
 // ---------------------------------------------------------------------------
+// Request owning block b (the last r with cu_blocks[r] <= b), found by the
+// whole wave: each step samples 64 evenly spaced entries of the remaining
+// span and keeps the one below the first sample past b, so up to 64 requests
+// take one round trip and up to 4096 two (a binary search takes log2 B
+// dependent ones).  b must be a block of the batch; the wave must be whole.
+__device__ __forceinline__ int block_owner(const int32_t* cu_blocks, int num_seqs, int64_t b,
+                                           int lane) {
+  int lo = 0, hi = num_seqs;  // cu_blocks[lo] <= b < cu_blocks[hi]
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const uint64_t le = __ballot(idx < hi && cu_blocks[idx] <= b);  // a prefix of lanes, lane 0 set
+    lo += (63 - __clzll((long long)le)) * step;
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
 template <bool COH>
 __device__ __forceinline__ void blockmean_one(const ScoreArgs& a, int64_t b, int lane) {
-  // request owning block b: last r with cu_blocks[r] <= b
-  int lo = 0, hi = a.num_seqs;  // invariant: cu_blocks[lo] <= b < cu_blocks[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
-  }
-  const int r = lo;
+  const int r = __builtin_amdgcn_readfirstlane(block_owner(a.cu_blocks, a.num_seqs, b, lane));
   const int s0 = a.cu_seqlens[r];
   const int L = a.cu_seqlens[r + 1] - s0;
   const int lb = (int)(b - a.cu_blocks[r]);
@@ -1168,17 +1180,10 @@ __global__ void __launch_bounds__(kSelectThreads) up_blockmean_select_kernel(Sco
     if (b < a.num_blocks) blockmean_one<true>(a, b, lane);
   }
   const int64_t b1 = min(b0 + BPW, a.num_blocks) - 1;
-  // requests owning the first and the last block here (the last r with
-  // cu_blocks[r] <= b); requests in between without blocks are skipped
-  auto owner = [&](int64_t b) {
-    int lo = 0, hi = a.num_seqs;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cu_blocks[mid] <= b) lo = mid; else hi = mid;
-    }
-    return lo;
-  };
-  const int r0 = owner(b0), r1 = owner(b1);
+  // requests owning the first and the last block here; requests in between
+  // without blocks are skipped
+  const int r0 = __builtin_amdgcn_readfirstlane(block_owner(a.cu_blocks, a.num_seqs, b0, lane));
+  const int r1 = __builtin_amdgcn_readfirstlane(block_owner(a.cu_blocks, a.num_seqs, b1, lane));
   for (int r = r0; r <= r1; ++r) {  // uniform over the workgroup
     const int64_t c0 = a.cu_blocks[r], c1 = a.cu_blocks[r + 1];
     if (c1 == c0) continue;
