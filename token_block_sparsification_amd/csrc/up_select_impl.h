@@ -28,7 +28,8 @@
 //      buffers, so clearing the next one overlaps building the current one.
 //   4. Blocks with score v* are tied; the lowest-index ones are kept until the
 //      mass reaches R: each thread takes a contiguous run of blocks, and one
-//      block-wide exclusive scan of the runs' tie counts ranks every tie.
+//      block-wide exclusive scan of the runs' tie counts ranks every tie (only
+//      when some tied blocks are dropped; the last radix pass counts them).
 // A request with at most STAGE blocks has its keys and fixed-point masses
 // computed once into LDS (every later pass reads them there); longer requests
 // recompute them from the scores in memory on every pass.  The workgroup
@@ -109,6 +110,7 @@ struct SelectShared {
   int all_optional;      // the optional mass never reaches R: keep every block
   uint64_t tie_mass;     // mass of one block at the cutoff key
   uint64_t tie_keep;     // how many tied blocks (lowest index first) are kept
+  uint32_t tie_count;    // optional blocks at the cutoff key
 };
 
 // Wave 0: scan the buckets from the top (descending keys) for the first
@@ -149,6 +151,7 @@ __device__ void pick_bucket(Shared& sh, int buf, int shift, int width, uint64_t 
     sh.above = acc;
     if (shift == 0) {
       const uint32_t c = sh.cnt[buf][bslot(digit)];
+      sh.tie_count = c;
       sh.tie_mass = c ? m[i] / c : 0;
       const uint64_t rest = need - acc;  // > 0, <= m[i]
       sh.tie_keep = sh.tie_mass ? (rest + sh.tie_mass - 1) / sh.tie_mass : c;
@@ -275,6 +278,7 @@ __device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared<N
     sh.all_optional = 0;
     sh.tie_mass = 0;
     sh.tie_keep = 0;
+    sh.tie_count = 0;
   }
   // the digits start at the highest bit where optional keys differ
   const uint32_t diff = kmin ^ kmax;
@@ -336,28 +340,33 @@ __device__ void select_impl(const SelectArgs& a, int req, int nb, SelectShared<N
   const uint32_t vstar = sh.prefix;
   const bool keep_all = sh.all_optional != 0;
   const uint64_t tie_keep = sh.tie_keep;
+  // ranks among the blocks at the cutoff key matter only when some of them
+  // are dropped (uniform over the workgroup)
+  const bool rank_ties = any_optional && !keep_all && tie_keep < (uint64_t)sh.tie_count;
   const int run = (nb + kSelectThreads - 1) / kSelectThreads;
   const int i0 = min(nb, tid * run), i1 = min(nb, i0 + run);
-  int my_ties = 0;
-  if (any_optional && !keep_all)
+  int64_t rank = 0;
+  if (rank_ties) {
+    int my_ties = 0;
     for (int i = i0; i < i1; ++i) {
       uint32_t key;
       uint64_t m;
       my_ties += (key_mass(i, key, m) && key == vstar) ? 1 : 0;
     }
-  // exclusive scan of the tie counts in thread (= block index) order
-  const int incl = (int)wave_scan_incl((uint32_t)my_ties);
-  if (lane == 63) sh.redi[wave] = incl;
-  __syncthreads();
-  int64_t rank = incl - my_ties;
-  for (int w = 0; w < wave; ++w) rank += sh.redi[w];
+    // exclusive scan of the tie counts in thread (= block index) order
+    const int incl = (int)wave_scan_incl((uint32_t)my_ties);
+    if (lane == 63) sh.redi[wave] = incl;
+    __syncthreads();
+    rank = incl - my_ties;
+    for (int w = 0; w < wave; ++w) rank += sh.redi[w];
+  }
   int kept_tokens = 0;
   for (int i = i0; i < i1; ++i) {
     uint32_t key;
     uint64_t m;
     const bool opt = key_mass(i, key, m);
-    bool keep = !opt || (any_optional && (keep_all || key > vstar));
-    if (opt && any_optional && !keep_all && key == vstar) keep = (uint64_t)(rank++) < tie_keep;
+    bool keep = !opt || (any_optional && (keep_all || key >= vstar));
+    if (rank_ties && opt && key == vstar) keep = (uint64_t)(rank++) < tie_keep;
     a.mask[cb0 + i] = keep ? 1 : 0;
     if (keep) kept_tokens += min(i * G + G, L) - i * G;
   }
